@@ -1,0 +1,309 @@
+"""Plain fp64 CPU oracle for the ISPA hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import this module:
+only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+use it. It shares no code with the HIP library (no kernels, helpers or
+constants); both sides only take their seeded inputs from ``workloads``.
+
+Source: the ISPA paper, "Towards Memory-Efficient Autoregressive Video
+Generation via Instance-Specific Parametric Absorption" (page text at
+paperpeel.com), and the reading notes on it at paper.gecl.asia ("Core Idea",
+"Method"). Everything here is the plain definition of what the method
+computes, written out directly in float64 with numpy:
+
+* attention over a KV set is ordinary softmax attention, computed separately
+  for the local set (sink + current), the history and the concatenated full
+  set. The full output is *not* obtained by merging partial results: the merge
+  is what the fast path does, and the oracle checks it instead of using it;
+* warmup statistics are plain sums over all warmup tokens;
+* the absorbed update is the closed-form ridge solution solved densely with
+  ``numpy.linalg.solve``;
+* the layer error is the residual of the absorbed reconstruction;
+* selection is a stable ascending sort.
+
+Conventions (row vectors): an attention output X = A_loc and Z = A_full are
+[N, h] with column head*d + j; the output projection is Y = X @ W_o^T with
+W_o stored as nn.Linear [out, in]. Inside the math W = W_o^T ([in, out]).
+
+Where the pages are silent the readings used are:
+  lambda is added unscaled to the summed statistics; LSE is natural log;
+  the softmax scale is 1/sqrt(d); no masking inside a chunk; an empty KV set
+  gives O = 0 and LSE = -inf; a layer whose solve failed or whose error is
+  NaN gets error +inf and is never selected; equal errors keep the lower
+  layer index first.
+
+Every function below is pinned by tests under ``tests/test_oracle_*.py``
+against closed forms, brute force and independent library routines.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+_BLOCK_Q = 512
+
+
+# ---------------------------------------------------------------------------
+# Attention (ISPA paper §3.1 item 1: A_full uses the whole history, A_loc
+# uses only current and sink tokens; §3.4: both come from one forward pass)
+# ---------------------------------------------------------------------------
+
+def softmax_attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                           scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax attention of one head over one KV set.
+
+    q [nq, d], k [n, d], v [n, d] -> (O [nq, d], LSE [nq]) with
+    s = scale * q k^T, m = max_j s, l = sum_j exp(s - m), O = sum_j
+    exp(s_j - m) v_j / l and LSE = m + ln l (natural log). n = 0 gives O = 0,
+    LSE = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nq, d = q.shape
+    n = k.shape[0]
+    out = np.zeros((nq, v.shape[1] if v.ndim == 2 else d), dtype=np.float64)
+    lse = np.full(nq, -np.inf, dtype=np.float64)
+    if n == 0:
+        return out, lse
+    for q0 in range(0, nq, _BLOCK_Q):
+        qb = q[q0:q0 + _BLOCK_Q]
+        s = scale * (qb @ k.T)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        l = p.sum(axis=1, keepdims=True)
+        out[q0:q0 + _BLOCK_Q] = (p @ v) / l
+        lse[q0:q0 + _BLOCK_Q] = m[:, 0] + np.log(l[:, 0])
+    return out, lse
+
+
+def multihead_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                        scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """q [nq, nh, d], k/v [n, nh, d] -> O [nq, nh*d] (column head*d + j),
+    LSE [nh, nq]."""
+    nq, nh, d = q.shape
+    o = np.zeros((nq, nh, d), dtype=np.float64)
+    lse = np.zeros((nh, nq), dtype=np.float64)
+    for hd in range(nh):
+        o[:, hd, :], lse[hd] = softmax_attention_head(q[:, hd, :], k[:, hd, :],
+                                                      v[:, hd, :], scale)
+    return o.reshape(nq, nh * d), lse
+
+
+def decomposable_attention(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist,
+                           scale: float) -> Dict[str, np.ndarray]:
+    """The three attention results the warmup needs, each computed directly.
+
+    local = attention over sink + current (A_loc), hist = attention over the
+    history alone, full = attention over the concatenated sink + history +
+    current (A_full). D = O_full - O_local is the discrepancy the absorption
+    fits (gecl.asia notes, "Method": the full-local output difference is the
+    supervision signal).
+    """
+    k_loc = np.concatenate([k_sink, k_cur], axis=0)
+    v_loc = np.concatenate([v_sink, v_cur], axis=0)
+    k_full = np.concatenate([k_sink, k_hist, k_cur], axis=0)
+    v_full = np.concatenate([v_sink, v_hist, v_cur], axis=0)
+    o_l, lse_l = multihead_attention(q, k_loc, v_loc, scale)
+    o_h, lse_h = multihead_attention(q, k_hist, v_hist, scale)
+    o_f, lse_f = multihead_attention(q, k_full, v_full, scale)
+    return {"o_local": o_l, "lse_local": lse_l, "o_hist": o_h,
+            "lse_hist": lse_h, "o_full": o_f, "lse_full": lse_f,
+            "d": o_f - o_l}
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
+    """Combine attention results over two disjoint KV sets (ISPA paper §3.4,
+    online-softmax decomposition via the log-sum-exp states).
+
+    o_* [nq, nh*d], lse_* [nh, nq]. Returns the result over the union. Used by
+    the tests to check the identity the fast path relies on; the oracle never
+    produces O_full this way.
+    """
+    nh, nq = lse_a.shape
+    d = o_a.shape[1] // nh
+    lse = np.logaddexp(lse_a, lse_b)
+    wa = np.where(np.isneginf(lse_a), 0.0, np.exp(lse_a - lse))
+    wb = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - lse))
+    oa = o_a.reshape(nq, nh, d)
+    ob = o_b.reshape(nq, nh, d)
+    o = wa.T[:, :, None] * oa + wb.T[:, :, None] * ob
+    return o.reshape(nq, nh * d), lse
+
+
+# ---------------------------------------------------------------------------
+# Warmup statistics (ISPA paper §3.1 item 2: "the accumulated dual-stream
+# activations serve as the basis for weight adaption")
+# ---------------------------------------------------------------------------
+
+def gram_statistics(xs: Sequence[np.ndarray], ds: Sequence[np.ndarray]
+                    ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Sums over every warmup step of G = X^T X, C = X^T D, E = D^T D.
+
+    xs, ds: per-step [N_s, h] local outputs and full-minus-local
+    differences. These three sums are all the solve and the error need.
+    """
+    h = xs[0].shape[1]
+    g = np.zeros((h, h))
+    c = np.zeros((h, h))
+    e = np.zeros((h, h))
+    for x, dd in zip(xs, ds):
+        x = np.asarray(x, dtype=np.float64)
+        dd = np.asarray(dd, dtype=np.float64)
+        g += x.T @ x
+        c += x.T @ dd
+        e += dd.T @ dd
+    return g, c, e
+
+
+# ---------------------------------------------------------------------------
+# Layer absorb (ISPA paper §3.1 item 2 and §3.2: a least-squares fit of a
+# modulation of the output projection so that the local output through
+# W + dW reproduces the full output through W; §4.1: a ridge parameter
+# lambda balances keeping the pre-trained weights; gecl.asia notes, "Method":
+# ridge regression on the attention output projection)
+# ---------------------------------------------------------------------------
+
+def ridge_delta_w(g: np.ndarray, c: np.ndarray, wo: np.ndarray, lam: float
+                  ) -> np.ndarray:
+    """dW minimising ||X (W + dW) - Z W||_F^2 + lam ||dW||_F^2.
+
+    With Z = X + D the minimiser is dW = (G + lam I)^{-1} C W (W = wo^T,
+    [in, out]). Returned in nn.Linear layout [out, in] (i.e. dW^T), like wo.
+    """
+    g = np.asarray(g, dtype=np.float64)
+    c = np.asarray(c, dtype=np.float64)
+    w = np.asarray(wo, dtype=np.float64).T
+    h = g.shape[0]
+    dw = np.linalg.solve(g + lam * np.eye(h), c @ w)
+    return dw.T.copy()
+
+
+def layer_error_from_stats(g, c, e, wo, dwo, lam: float) -> Tuple[float, float]:
+    """Reconstruction error of the absorbed layer from the statistics.
+
+    eps_abs = ||X (W + dW) - Z W||_F^2 over all warmup tokens
+            = tr(dW^T G dW) - 2 tr(dW^T C W) + tr(W^T E W)
+    eps_rel = eps_abs / ||Z W||_F^2, with Z^T Z = G + C + C^T + E.
+    (ISPA paper §3.3: the error metric used to rank layers; its definition is
+    lost from the page text, this is the residual of the reconstruction named
+    in the §3.2 title.)
+    """
+    g = np.asarray(g, dtype=np.float64)
+    c = np.asarray(c, dtype=np.float64)
+    e = np.asarray(e, dtype=np.float64)
+    w = np.asarray(wo, dtype=np.float64).T
+    dw = np.asarray(dwo, dtype=np.float64).T
+    quad = np.sum(dw * (g @ dw))
+    cross = np.sum(dw * (c @ w))
+    tew = np.sum(w * (e @ w))
+    eps_abs = quad - 2.0 * cross + tew
+    zz = g + c + c.T + e
+    denom = np.sum(w * (zz @ w))
+    eps_rel = eps_abs / denom if denom > 0 else (0.0 if eps_abs == 0 else math.inf)
+    return float(eps_abs), float(eps_rel)
+
+
+def layer_error_direct(x_all, z_all, wo, dwo) -> Tuple[float, float]:
+    """The same error evaluated on the stacked warmup activations."""
+    w = np.asarray(wo, dtype=np.float64).T
+    dw = np.asarray(dwo, dtype=np.float64).T
+    x_all = np.asarray(x_all, dtype=np.float64)
+    z_all = np.asarray(z_all, dtype=np.float64)
+    target = z_all @ w
+    r = x_all @ (w + dw) - target
+    eps_abs = float(np.sum(r * r))
+    denom = float(np.sum(target * target))
+    return eps_abs, (eps_abs / denom if denom > 0 else
+                     (0.0 if eps_abs == 0 else math.inf))
+
+
+# ---------------------------------------------------------------------------
+# Dynamic layer selection (ISPA paper §3.3: rank layers by ascending error,
+# the K lowest become L-layers)
+# ---------------------------------------------------------------------------
+
+def select_layers(eps: np.ndarray, k: int,
+                  valid: Optional[np.ndarray] = None) -> np.ndarray:
+    """int32 [L] with 1 for the min(K, #valid) lowest-error layers.
+
+    Invalid layers (failed solve) and NaN errors count as +inf and are never
+    selected; equal errors keep the lower layer index first.
+    """
+    eps = np.array(eps, dtype=np.float64)
+    n = eps.shape[0]
+    if valid is None:
+        valid = np.ones(n, dtype=bool)
+    key = np.where(valid & ~np.isnan(eps), eps, np.inf)
+    order = np.argsort(key, kind="stable")
+    sel = np.zeros(n, dtype=np.int32)
+    taken = 0
+    for idx in order:
+        if taken >= k or not np.isfinite(key[idx]):
+            break
+        sel[idx] = 1
+        taken += 1
+    return sel
+
+
+# ---------------------------------------------------------------------------
+# Weight injection (ISPA paper §3.3: W_new = W + dW, updated in place in the
+# weight's own storage type, bf16 here)
+# ---------------------------------------------------------------------------
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Correctly rounded fp64 -> bf16 (nearest, ties to even), returned as
+    fp64 values.
+
+    A bf16 has an 8-bit significand: for |x| = m * 2^ex with m in [0.5, 1)
+    the representable spacing is 2^(ex-8) (never below the subnormal spacing
+    2^-133). Dividing by that power of two is exact in fp64, so rounding the
+    quotient to an integer with ties-to-even (numpy.rint) and scaling back is
+    the exact rounding. Magnitudes that round to 2^128 or more overflow to
+    inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    _, ex = np.frexp(ax)
+    ulp = np.ldexp(1.0, np.maximum(ex - 8, -133))
+    mag = np.rint(ax / ulp) * ulp
+    mag = np.where(mag >= 2.0 ** 128, np.inf, mag)
+    out = np.copysign(mag, x)
+    keep = (ax == 0.0) | ~np.isfinite(x)
+    return np.where(keep, x, out)
+
+
+def apply_delta(wo: np.ndarray, dwo: np.ndarray) -> np.ndarray:
+    """bf16 storage of W_o + dW (both [out, in])."""
+    return bf16_round(np.asarray(wo, dtype=np.float64) +
+                      np.asarray(dwo, dtype=np.float64))
+
+
+def project(x: np.ndarray, wo: np.ndarray) -> np.ndarray:
+    """L-layer output projection Y = X W^T for x [N, in], wo [out, in]
+    (ISPA paper §3.1 item 3: L-layers use local attention with W_new)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(wo, dtype=np.float64).T
+
+
+# ---------------------------------------------------------------------------
+# Whole warmup (ISPA paper §3.1 items 1-3) for small cases
+# ---------------------------------------------------------------------------
+
+def run_warmup_layer(steps, wo, lam: float, scale: float):
+    """steps: iterable of workloads.StepInputs for one layer.
+    Returns dict with stacked X/Z, statistics, dW and the error."""
+    xs, ds, zs = [], [], []
+    for st in steps:
+        r = decomposable_attention(st.q, st.k_sink, st.v_sink, st.k_cur,
+                                   st.v_cur, st.k_hist, st.v_hist, scale)
+        xs.append(r["o_local"])
+        ds.append(r["d"])
+        zs.append(r["o_full"])
+    g, c, e = gram_statistics(xs, ds)
+    dw = ridge_delta_w(g, c, wo, lam)
+    eps_abs, eps_rel = layer_error_from_stats(g, c, e, wo, dw, lam)
+    return {"x_all": np.concatenate(xs), "z_all": np.concatenate(zs),
+            "d_all": np.concatenate(ds), "g": g, "c": c, "e": e, "dw": dw,
+            "eps_abs": eps_abs, "eps_rel": eps_rel}
