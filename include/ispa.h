@@ -1,0 +1,185 @@
+/*
+ * ispa.h - C ABI of the ISPA hot path on AMD Instinct MI355X (gfx950).
+ *
+ * ISPA = Instance-Specific Parametric Absorption, from the paper "Towards
+ * Memory-Efficient Autoregressive Video Generation via Instance-Specific
+ * Parametric Absorption". During a short warmup every attention layer runs
+ * as a full-history layer while the local-only output (sink frame + current
+ * frames) is collected beside it (§3.1 item 1, §3.4). At the end of warmup a
+ * closed-form least-squares update dW of each layer's output projection is
+ * fitted so that the local output through W + dW reproduces the full output
+ * through W (§3.1 item 2, §3.2, ridge parameter of §4.1); layers are ranked
+ * by their reconstruction error and the K best take the update in place and
+ * drop their history KV (§3.3). L-layers then run local attention only with
+ * W + dW (§3.1 item 3).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless stated otherwise; the caller owns
+ *    every buffer. The library never allocates, frees or synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns immediately. Argument checks are synchronous: on
+ *    any error status nothing has been enqueued.
+ *  - bf16 tensors are passed as raw 16-bit storage (void*).
+ *  - Row-major, contiguous. Weight-shaped matrices (W_o, dW) use the
+ *    nn.Linear layout [out, in]; the activations X (local attention output)
+ *    and Z (full attention output) are [tokens, hidden] with column
+ *    head * head_dim + j, and the projection is Y = X W^T.
+ *  - Device pointers must be 16-byte aligned (ISPA_ERR_ALIGN otherwise).
+ *  - Calls on one stream execute in order; calls that write the same buffers
+ *    from different streams must be ordered by the caller.
+ */
+#ifndef ISPA_H_
+#define ISPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ISPA_OK = 0,
+  ISPA_ERR_NULL = 1,        /* a required pointer is NULL */
+  ISPA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  ISPA_ERR_UNSUPPORTED = 3, /* a valid but unsupported configuration */
+  ISPA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  ISPA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+  ISPA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+};
+
+/* Static text for a status code (never NULL). */
+const char* ispa_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int ispa_version(void);
+
+/*
+ * Decomposable attention (§3.1 item 1 and §3.4).
+ *
+ * For each head and query row q of the chunk, with s_j = sm_scale * q . k_j:
+ *   local   = softmax attention over the sink and current keys (A_loc),
+ *   history = softmax attention over the history keys,
+ *   full    = softmax attention over sink + history + current (A_full),
+ * all from one pass over the KV: the local and history partial results are
+ * merged through their log-sum-exp states. No mask inside the chunk.
+ *
+ * q                [n_q, n_heads, head_dim] bf16 (post-RoPE).
+ * k_/v_sink        [n_sink, n_heads, head_dim] bf16; k_/v_cur [n_cur, ...];
+ * k_/v_hist        [n_hist, ...]. Segments may live in separate buffers.
+ * head_dim         64 or 128 (ISPA_ERR_UNSUPPORTED otherwise).
+ * sm_scale         softmax scale (> 0, finite), normally 1/sqrt(head_dim).
+ * Outputs (any may be NULL = not produced; at least one non-NULL):
+ *   o_local, o_hist, o_full, d_out   [n_q, n_heads * head_dim] bf16,
+ *   lse_local, lse_hist, lse_full    [n_heads, n_q] fp32, natural log.
+ * d_out = O_full - O_local, formed in fp32 against the bf16-rounded O_local
+ *   that o_local holds, so X + D tracks O_full as closely as bf16 allows.
+ * An empty history (n_hist = 0) gives o_hist = 0, lse_hist = -inf,
+ *   o_full = o_local and d_out = 0. n_sink + n_cur must be >= 1.
+ * When only o_full / lse_full are requested the KV is traversed once
+ *   without the split.
+ * Errors: ISPA_ERR_NULL for a NULL q, a NULL segment pointer with a non-zero
+ *   length, or no output; ISPA_ERR_SHAPE for negative sizes, n_heads < 1,
+ *   n_sink + n_cur == 0 or a non-positive scale; ISPA_ERR_UNSUPPORTED for
+ *   another head_dim.
+ */
+int ispa_attn_decomp(const void* q, int64_t n_q,
+                     const void* k_sink, const void* v_sink, int64_t n_sink,
+                     const void* k_cur, const void* v_cur, int64_t n_cur,
+                     const void* k_hist, const void* v_hist, int64_t n_hist,
+                     int n_heads, int head_dim, float sm_scale,
+                     void* o_local, float* lse_local,
+                     void* o_hist, float* lse_hist,
+                     void* o_full, float* lse_full,
+                     void* d_out, void* stream);
+
+/*
+ * Warmup statistics (§3.1 item 2: the accumulated dual-stream activations).
+ *
+ * For each of n_batch independent problems b (e.g. layers):
+ *   G[b] (+)= X[b]^T X[b],  C[b] (+)= X[b]^T D[b],  E[b] (+)= D[b]^T D[b]
+ * x, d   [n_batch][n_tok, h] bf16 (X = O_local, D = O_full - O_local).
+ * G, C, E [n_batch][h, h] fp32; E may be NULL. On return G and E are full
+ *   symmetric matrices. zero_first != 0 overwrites instead of adding.
+ * Summation order is fixed: results are bitwise reproducible.
+ * n_tok may be 0 (adds nothing, or zeroes with zero_first).
+ * Errors: ISPA_ERR_NULL (x, d, G, C), ISPA_ERR_SHAPE (h < 1, n_tok < 0,
+ *   n_batch < 1), ISPA_ERR_UNSUPPORTED (h not a multiple of 8).
+ */
+int ispa_gram_accumulate(const void* x, const void* d, int64_t n_tok, int h,
+                         int n_batch, float* G, float* C, float* E,
+                         int zero_first, void* stream);
+
+/*
+ * Closed-form absorb (§3.2, §4.1): for each layer l,
+ *   dW = argmin ||X (W + dW) - Z W||_F^2 + lambda ||dW||_F^2
+ *      = (G + lambda I)^{-1} C W        (W = Wo^T, math layout [in, out]),
+ * solved by a blocked fp32 Cholesky factorisation of G + lambda I and two
+ * triangular solves. lambda is added unscaled to the summed statistics.
+ * G, C     [n_layers][h, h] fp32 (read only).
+ * Wo       [n_layers][h, h] bf16, nn.Linear layout (read only).
+ * dW       [n_layers][h, h] fp32 output, nn.Linear layout (like Wo).
+ * info     [n_layers] int32 device output: 0 = solved; j > 0 = the leading
+ *          minor of order j of G + lambda I is not positive definite (dW of
+ *          that layer is then meaningless, but finite work was done).
+ * workspace: device buffer of at least ispa_ridge_workspace_bytes(n_layers,
+ *          h) bytes. After the call it holds C W (used by ispa_layer_score).
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (n_layers < 1, h < 1, lambda < 0 or
+ *   not finite), ISPA_ERR_UNSUPPORTED (h not a multiple of 8),
+ *   ISPA_ERR_WORKSPACE.
+ */
+size_t ispa_ridge_workspace_bytes(int n_layers, int h);
+int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C,
+                     const void* Wo, float lambda, float* dW, int* info,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Layer error and dynamic selection (§3.3). For each layer, over all warmup
+ * tokens:
+ *   eps_abs = ||X (W + dW) - Z W||_F^2
+ *           = tr(W^T E W) - tr(dW^T C W) - lambda ||dW||_F^2  (at the ridge
+ *             optimum), Z = X + D,
+ *   eps_rel = eps_abs / ||Z W||_F^2, ||Z W||^2 = tr(W^T (G + C + C^T + E) W);
+ *   eps_rel = 0 when both are 0, +inf when only the denominator is 0.
+ * Layers with info != 0 or a NaN error get +inf and are never selected.
+ * selected[l] = 1 for the min(K, #valid) layers with the lowest eps_rel
+ *   (equal errors: lower layer index first), else 0.
+ * workspace: the workspace of the ispa_ridge_solve call that produced dW, on
+ *   the same stream and unchanged since (it reads C W from it and reuses the
+ *   rest as scratch).
+ * eps_abs, eps_rel [n_layers] fp64, selected [n_layers] int32: device outputs.
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (K < 0, ...), ISPA_ERR_WORKSPACE.
+ */
+int ispa_layer_score(int n_layers, int h, const float* G, const float* C,
+                     const float* E, const void* Wo, const float* dW,
+                     float lambda, const int* info, int K,
+                     void* workspace, size_t ws_bytes,
+                     double* eps_abs, double* eps_rel, int* selected,
+                     void* stream);
+
+/*
+ * Weight injection (§3.3: W_new = W + dW, updated in place).
+ * For every layer with selected[l] != 0 (device int32 [n_layers]):
+ *   Wo[l] = bf16(Wo[l] + dW[l]), correctly rounded (nearest, ties to even)
+ * from the exact sum. Other layers are untouched.
+ * Wo [n_layers][h, h] bf16 in/out; dW [n_layers][h, h] fp32.
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE, ISPA_ERR_UNSUPPORTED (h % 8 != 0).
+ */
+int ispa_apply_dW(int n_layers, int h, const int* selected, const float* dW,
+                  void* Wo, void* stream);
+
+/*
+ * L-layer output projection (§3.1 item 3): y = x w^T.
+ * x [n, h_in] bf16, w [h_out, h_in] bf16 (nn.Linear layout), y [n, h_out]
+ * bf16 (fp32 accumulation, round to nearest even). No bias.
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE, ISPA_ERR_UNSUPPORTED (h_in or h_out
+ *   not a multiple of 8).
+ */
+int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in,
+                 int h_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISPA_H_ */

@@ -1,0 +1,63 @@
+// Device-side helpers shared by the ISPA HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ispa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 <-> fp32 on raw 16-bit storage.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (gfx950 lowers the cast to
+// v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+// Interleave 16-bit halves of two words: (lo16(a), lo16(b)) and (hi16(a), hi16(b)).
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate. Operand lane layout used throughout:
+// lane l holds A[m = l%32][k-slot j] and B[k-slot j][n = l%32] for j = 0..7 of
+// k-half l/32; the result lane l, register i holds D[m = 8*(i/4) + 4*(l/32) +
+// (i%4)][n = l%32].
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x2 fp32 MFMA: lane l holds A[m = l%32][k = l/32], B[k = l/32][n = l%32].
+__device__ __forceinline__ f32x16 mfma32x32x2f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X. Remap
+// the hardware block id so that consecutive logical work items land on the
+// same XCD (and share its L2): logical id = start(xcd) + bid / 8.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int xcd = bid % 8, slot = bid / 8;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+}  // namespace ispa

@@ -1,0 +1,299 @@
+// C ABI of the ISPA hot path: argument validation, workspace layout and the
+// launch sequence of each entry point. Declarations and contracts are in
+// include/ispa.h.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "ispa.h"
+#include "ispa_internal.h"
+
+namespace {
+
+using ispa::kCholBlock;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ISPA_OK : ISPA_ERR_HIP; }
+
+#define ISPA_TRY(expr)                       \
+  do {                                       \
+    const hipError_t e_ = (expr);            \
+    if (e_ != hipSuccess) return ISPA_ERR_HIP; \
+  } while (0)
+
+size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+struct RidgeWs {
+  float* L;       // [n_layers][h, h] Cholesky factor (later: W W^T for scoring)
+  float* R;       // [n_layers][h, h] right-hand side -> dW (math layout)
+  float* Bt;      // [n_layers][h, h] (C W)^T in nn.Linear layout
+  float* Linv;    // [n_layers][h, 128] inverses of the diagonal blocks
+  double* part;   // layer-score partial sums
+  size_t bytes;
+};
+
+RidgeWs ridge_layout(void* base, int n_layers, int h) {
+  RidgeWs w{};
+  const size_t hh = static_cast<size_t>(h) * h * n_layers * sizeof(float);
+  const size_t lin = static_cast<size_t>(h) * kCholBlock * n_layers * sizeof(float);
+  const size_t part = ispa::layer_score_partial_count(n_layers, h) * sizeof(double);
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  w.L = reinterpret_cast<float*>(p + off);    off = align_up(off + hh);
+  w.R = reinterpret_cast<float*>(p + off);    off = align_up(off + hh);
+  w.Bt = reinterpret_cast<float*>(p + off);   off = align_up(off + hh);
+  w.Linv = reinterpret_cast<float*>(p + off); off = align_up(off + lin);
+  w.part = reinterpret_cast<double*>(p + off); off = align_up(off + part);
+  w.bytes = off;
+  return w;
+}
+
+// One fp32 GEMM over all layers: operand (i, j) at ptr[i * s0 + j * s1].
+hipError_t gemm(int M, int N, int K, const void* A, int64_t a_s0, int64_t a_s1, int64_t a_batch,
+                bool a_bf16, const void* B, int64_t b_s0, int64_t b_s1, int64_t b_batch,
+                bool b_bf16, float* C, int64_t ldc, int64_t c_batch, float alpha, float beta,
+                int batch, bool tri, hipStream_t s) {
+  ispa::GemmF32Params p{};
+  p.M = M; p.N = N; p.K = K;
+  p.A = A; p.a_s0 = a_s0; p.a_s1 = a_s1; p.a_batch = a_batch; p.a_bf16 = a_bf16;
+  p.B = B; p.b_s0 = b_s0; p.b_s1 = b_s1; p.b_batch = b_batch; p.b_bf16 = b_bf16;
+  p.Cm = C; p.ldc = ldc; p.c_batch = c_batch;
+  p.alpha = alpha; p.beta = beta; p.batch = batch; p.tri = tri ? 1 : 0;
+  return ispa::launch_gemm_f32(p, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ispa_status_string(int status) {
+  switch (status) {
+    case ISPA_OK: return "ok";
+    case ISPA_ERR_NULL: return "required pointer is NULL";
+    case ISPA_ERR_SHAPE: return "size out of range or inconsistent";
+    case ISPA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ISPA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case ISPA_ERR_WORKSPACE: return "workspace missing or too small";
+    case ISPA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int ispa_version(void) { return 100; }
+
+int ispa_attn_decomp(const void* q, int64_t n_q, const void* k_sink, const void* v_sink,
+                     int64_t n_sink, const void* k_cur, const void* v_cur, int64_t n_cur,
+                     const void* k_hist, const void* v_hist, int64_t n_hist, int n_heads,
+                     int head_dim, float sm_scale, void* o_local, float* lse_local, void* o_hist,
+                     float* lse_hist, void* o_full, float* lse_full, void* d_out, void* stream) {
+  if (n_q < 0 || n_sink < 0 || n_cur < 0 || n_hist < 0 || n_heads < 1) return ISPA_ERR_SHAPE;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return ISPA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return ISPA_ERR_UNSUPPORTED;
+  if (!q && n_q > 0) return ISPA_ERR_NULL;
+  if ((n_sink > 0 && (!k_sink || !v_sink)) || (n_cur > 0 && (!k_cur || !v_cur)) ||
+      (n_hist > 0 && (!k_hist || !v_hist)))
+    return ISPA_ERR_NULL;
+  if (!o_local && !lse_local && !o_hist && !lse_hist && !o_full && !lse_full && !d_out)
+    return ISPA_ERR_NULL;
+  if (n_sink + n_cur < 1) return ISPA_ERR_SHAPE;
+  const void* ptrs[] = {q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, o_local, lse_local,
+                        o_hist, lse_hist, o_full, lse_full, d_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return ISPA_ERR_ALIGN;
+  const int64_t qtiles = (n_q + ispa::attn_q_tile() - 1) / ispa::attn_q_tile();
+  if (qtiles * n_heads > INT32_MAX) return ISPA_ERR_SHAPE;
+  if (n_q == 0) return ISPA_OK;
+
+  ispa::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k[0] = static_cast<const uint16_t*>(k_sink);
+  p.v[0] = static_cast<const uint16_t*>(v_sink);
+  p.n[0] = n_sink;
+  p.k[1] = static_cast<const uint16_t*>(k_cur);
+  p.v[1] = static_cast<const uint16_t*>(v_cur);
+  p.n[1] = n_cur;
+  p.k[2] = static_cast<const uint16_t*>(k_hist);
+  p.v[2] = static_cast<const uint16_t*>(v_hist);
+  p.n[2] = n_hist;
+  p.n_q = n_q;
+  p.n_heads = n_heads;
+  p.scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  p.o_local = static_cast<uint16_t*>(o_local);
+  p.lse_local = lse_local;
+  p.o_hist = static_cast<uint16_t*>(o_hist);
+  p.lse_hist = lse_hist;
+  p.o_full = static_cast<uint16_t*>(o_full);
+  p.lse_full = lse_full;
+  p.d_out = static_cast<uint16_t*>(d_out);
+  p.n_qtiles = static_cast<int>(qtiles);
+  const bool only_full = !o_local && !lse_local && !o_hist && !lse_hist && !d_out;
+  p.mode = only_full ? 1 : 0;
+  p.need_hist = (o_hist || lse_hist || o_full || lse_full || d_out) ? 1 : 0;
+  return hip_status(ispa::launch_attn_decomp(p, head_dim, as_stream(stream)));
+}
+
+int ispa_gram_accumulate(const void* x, const void* d, int64_t n_tok, int h, int n_batch,
+                         float* G, float* C, float* E, int zero_first, void* stream) {
+  if (!x || !d || !G || !C) return ISPA_ERR_NULL;
+  if (h < 1 || n_tok < 0 || n_batch < 1) return ISPA_ERR_SHAPE;
+  if (h % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(d) || !aligned16(G) || !aligned16(C) || (E && !aligned16(E)))
+    return ISPA_ERR_ALIGN;
+  ispa::GramParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.d = static_cast<const uint16_t*>(d);
+  p.n_tok = n_tok;
+  p.h = h;
+  p.batch = n_batch;
+  p.G = G;
+  p.C = C;
+  p.E = E;
+  p.zero_first = zero_first ? 1 : 0;
+  if (n_tok == 0 && !zero_first) return ISPA_OK;
+  return hip_status(ispa::launch_gram(p, as_stream(stream)));
+}
+
+size_t ispa_ridge_workspace_bytes(int n_layers, int h) {
+  if (n_layers < 1 || h < 1) return 0;
+  return ridge_layout(nullptr, n_layers, h).bytes;
+}
+
+int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const void* Wo,
+                     float lambda, float* dW, int* info, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  if (!G || !C || !Wo || !dW || !info) return ISPA_ERR_NULL;
+  if (n_layers < 1 || h < 1 || !(lambda >= 0.f) || !isfinite(lambda)) return ISPA_ERR_SHAPE;
+  if (h % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < ispa_ridge_workspace_bytes(n_layers, h)) return ISPA_ERR_WORKSPACE;
+  if (!aligned16(G) || !aligned16(C) || !aligned16(Wo) || !aligned16(dW) || !aligned16(info) ||
+      !aligned16(workspace))
+    return ISPA_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  const RidgeWs w = ridge_layout(workspace, n_layers, h);
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
+  const int L = n_layers;
+  const int nblk = (h + kCholBlock - 1) / kCholBlock;
+
+  // Cholesky of M = G + lambda I, one 128-column block at a time.
+  ISPA_TRY(ispa::launch_copy_add_diag(G, w.L, h, L, lambda, s));
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int k0 = kb * kCholBlock;
+    const int nbk = (h - k0) < kCholBlock ? (h - k0) : kCholBlock;
+    const int rem = h - k0 - nbk;
+    ISPA_TRY(ispa::launch_potrf_block(w.L, w.Linv, h, k0, nbk, L, info, kb == 0, s));
+    if (rem > 0) {
+      float* panel = w.L + static_cast<int64_t>(k0 + nbk) * h + k0;
+      const float* linv = w.Linv + static_cast<int64_t>(k0) * kCholBlock;
+      // panel <- panel * Linv_kk^T   (in place: one tile column)
+      ISPA_TRY(gemm(rem, nbk, nbk, panel, h, 1, hh, false, linv, 1, kCholBlock, lb, false, panel,
+                    h, hh, 1.f, 0.f, L, false, s));
+      // trailing <- trailing - panel panel^T   (lower 128-tiles only)
+      ISPA_TRY(gemm(rem, rem, nbk, panel, h, 1, hh, false, panel, 1, h, hh, false,
+                    w.L + static_cast<int64_t>(k0 + nbk) * h + k0 + nbk, h, hh, -1.f, 1.f, L,
+                    true, s));
+    }
+  }
+
+  // R = C W (math layout [in, out]); W(k, o) = Wo[o][k]. Keep (C W)^T for scoring.
+  ISPA_TRY(gemm(h, h, h, C, h, 1, hh, false, Wo, 1, h, hh, true, w.R, h, hh, 1.f, 0.f, L, false,
+                s));
+  ISPA_TRY(ispa::launch_transpose(w.R, w.Bt, h, L, s));
+
+  // Forward substitution L Z = R, block rows top to bottom.
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int k0 = kb * kCholBlock;
+    const int nbk = (h - k0) < kCholBlock ? (h - k0) : kCholBlock;
+    const int rem = h - k0 - nbk;
+    float* rk = w.R + static_cast<int64_t>(k0) * h;
+    const float* linv = w.Linv + static_cast<int64_t>(k0) * kCholBlock;
+    ISPA_TRY(gemm(nbk, h, nbk, linv, kCholBlock, 1, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
+                  0.f, L, false, s));
+    if (rem > 0) {
+      ISPA_TRY(gemm(rem, h, nbk, w.L + static_cast<int64_t>(k0 + nbk) * h + k0, h, 1, hh, false,
+                    rk, h, 1, hh, false, rk + static_cast<int64_t>(nbk) * h, h, hh, -1.f, 1.f, L,
+                    false, s));
+    }
+  }
+  // Back substitution L^T dW = Z, block rows bottom to top.
+  for (int kb = nblk - 1; kb >= 0; --kb) {
+    const int k0 = kb * kCholBlock;
+    const int nbk = (h - k0) < kCholBlock ? (h - k0) : kCholBlock;
+    float* rk = w.R + static_cast<int64_t>(k0) * h;
+    const float* linv = w.Linv + static_cast<int64_t>(k0) * kCholBlock;
+    ISPA_TRY(gemm(nbk, h, nbk, linv, 1, kCholBlock, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
+                  0.f, L, false, s));
+    if (k0 > 0) {
+      // R[0:k0] -= L[k0:k0+nbk, 0:k0]^T X_k
+      ISPA_TRY(gemm(k0, h, nbk, w.L + static_cast<int64_t>(k0) * h, 1, h, hh, false, rk, h, 1, hh,
+                    false, w.R, h, hh, -1.f, 1.f, L, false, s));
+    }
+  }
+  ISPA_TRY(ispa::launch_transpose(w.R, dW, h, L, s));
+  return ISPA_OK;
+}
+
+int ispa_layer_score(int n_layers, int h, const float* G, const float* C, const float* E,
+                     const void* Wo, const float* dW, float lambda, const int* info, int K,
+                     void* workspace, size_t ws_bytes, double* eps_abs, double* eps_rel,
+                     int* selected, void* stream) {
+  if (!G || !C || !E || !Wo || !dW || !eps_abs || !eps_rel || !selected) return ISPA_ERR_NULL;
+  if (n_layers < 1 || h < 1 || K < 0 || !(lambda >= 0.f) || !isfinite(lambda))
+    return ISPA_ERR_SHAPE;
+  if (h % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < ispa_ridge_workspace_bytes(n_layers, h)) return ISPA_ERR_WORKSPACE;
+  if (!aligned16(G) || !aligned16(C) || !aligned16(E) || !aligned16(Wo) || !aligned16(dW) ||
+      !aligned16(workspace) || !aligned16(eps_abs) || !aligned16(eps_rel) || !aligned16(selected) ||
+      (info && !aligned16(info)))
+    return ISPA_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  const RidgeWs w = ridge_layout(workspace, n_layers, h);
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  // P = W W^T (math W = Wo^T): P(i, j) = sum_o Wo[o][i] Wo[o][j]; lower tiles.
+  ISPA_TRY(gemm(h, h, h, Wo, 1, h, hh, true, Wo, h, 1, hh, true, w.L, h, hh, 1.f, 0.f, n_layers,
+                true, s));
+  ispa::ScoreParams p{};
+  p.n_layers = n_layers;
+  p.h = h;
+  p.G = G;
+  p.C = C;
+  p.E = E;
+  p.Wo = static_cast<const uint16_t*>(Wo);
+  p.dW = dW;
+  p.lam = lambda;
+  p.info = info;
+  p.K = K;
+  p.partial = w.part;
+  p.eps_abs = eps_abs;
+  p.eps_rel = eps_rel;
+  p.selected = selected;
+  return hip_status(ispa::launch_score(p, w.L, w.Bt, s));
+}
+
+int ispa_apply_dW(int n_layers, int h, const int* selected, const float* dW, void* Wo,
+                  void* stream) {
+  if (!selected || !dW || !Wo) return ISPA_ERR_NULL;
+  if (n_layers < 1 || h < 1) return ISPA_ERR_SHAPE;
+  if (h % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (!aligned16(selected) || !aligned16(dW) || !aligned16(Wo)) return ISPA_ERR_ALIGN;
+  return hip_status(ispa::launch_apply_dw(n_layers, h, selected, dW,
+                                          static_cast<uint16_t*>(Wo), as_stream(stream)));
+}
+
+int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in, int h_out,
+                 void* stream) {
+  if (!x || !w || !y) return ISPA_ERR_NULL;
+  if (n < 0 || h_in < 1 || h_out < 1) return ISPA_ERR_SHAPE;
+  if (h_in % 8 != 0 || h_out % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return ISPA_ERR_ALIGN;
+  if (n == 0) return ISPA_OK;
+  return hip_status(ispa::launch_project(static_cast<const uint16_t*>(x),
+                                         static_cast<const uint16_t*>(w),
+                                         static_cast<uint16_t*>(y), n, h_in, h_out,
+                                         as_stream(stream)));
+}
+
+}  // extern "C"

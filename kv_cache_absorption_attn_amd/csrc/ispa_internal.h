@@ -1,0 +1,106 @@
+// Internal launch interface between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ispa {
+
+// ---------------------------------------------------------------- attention
+struct AttnParams {
+  const uint16_t* q;         // [n_q, n_heads, D] bf16
+  const uint16_t* k[3];      // segments: 0 sink, 1 current, 2 history
+  const uint16_t* v[3];
+  int64_t n[3];
+  int64_t n_q;
+  int n_heads;
+  float scale_log2;          // softmax scale * log2(e)
+  uint16_t* o_local;         // [n_q, n_heads*D] bf16 (any may be null)
+  float* lse_local;          // [n_heads, n_q]
+  uint16_t* o_hist;
+  float* lse_hist;
+  uint16_t* o_full;
+  float* lse_full;
+  uint16_t* d_out;
+  int n_qtiles;
+  int mode;                  // 0: local / history split + merge; 1: one pass (full only)
+  int need_hist;             // split mode: history phase and merge needed
+};
+hipError_t launch_attn_decomp(const AttnParams& p, int head_dim, hipStream_t stream);
+int attn_q_tile();
+
+// ---------------------------------------------------------------- Gram
+struct GramParams {
+  const uint16_t* x;         // [batch][n_tok, h] bf16
+  const uint16_t* d;
+  int64_t n_tok;
+  int h;
+  int batch;
+  float* G;                  // [batch][h, h] fp32
+  float* C;
+  float* E;                  // may be null
+  int zero_first;
+};
+hipError_t launch_gram(const GramParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- fp32 GEMM
+// C[b](m, n) = alpha * sum_k A[b](m, k) B[b](k, n) + beta * C[b](m, n)
+// Operand element (i, j) lives at ptr[i * s0 + j * s1]; one of the two
+// strides of A and of B must be 1 (that dimension is loaded contiguously).
+// C is row-major with leading dimension ldc. A may be bf16 (a_bf16 = 1).
+struct GemmF32Params {
+  int M, N, K;
+  const void* A;
+  int64_t a_s0, a_s1, a_batch;
+  int a_bf16;
+  const void* B;
+  int64_t b_s0, b_s1, b_batch;
+  int b_bf16;
+  float* Cm;
+  int64_t ldc, c_batch;
+  float alpha, beta;
+  int batch;
+  int tri;                   // 0 all tiles; 1 only tiles with tile_m >= tile_n
+};
+hipError_t launch_gemm_f32(const GemmF32Params& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- ridge pieces
+hipError_t launch_copy_add_diag(const float* G, float* L, int h, int batch, float lam,
+                                hipStream_t stream);
+// Diagonal block [k0, k0+nb) of L (nb <= 128): factor in place, write its
+// inverse to Linv + k0 * 128 ([nb][128] row-major), record failures in info.
+hipError_t launch_potrf_block(float* L, float* Linv, int h, int k0, int nb, int batch,
+                              int* info, int info_first, hipStream_t stream);
+// dst[b] = src[b]^T for h x h fp32 matrices.
+hipError_t launch_transpose(const float* src, float* dst, int h, int batch, hipStream_t stream);
+constexpr int kCholBlock = 128;
+
+// ---------------------------------------------------------------- score / select / apply
+struct ScoreParams {
+  int n_layers, h;
+  const float* G;
+  const float* C;
+  const float* E;
+  const uint16_t* Wo;        // [L][out, in] bf16
+  const float* dW;           // [L][out, in] fp32
+  float lam;
+  const int* info;
+  int K;
+  double* partial;           // workspace for per-tile partial sums
+  double* eps_abs;
+  double* eps_rel;
+  int* selected;
+};
+// P = W W^T (lower 128-tiles valid), Bt = (C W)^T in nn.Linear layout.
+hipError_t launch_score(const ScoreParams& p, const float* P, const float* Bt,
+                        hipStream_t stream);
+size_t layer_score_partial_count(int n_layers, int h);
+
+hipError_t launch_apply_dw(int n_layers, int h, const int* selected, const float* dW,
+                           uint16_t* Wo, hipStream_t stream);
+
+// ---------------------------------------------------------------- projection
+hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
+                          int h_in, int h_out, hipStream_t stream);
+
+}  // namespace ispa

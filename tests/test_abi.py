@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments synchronously with the documented status codes.
+
+No call here reaches a kernel launch: every call is built to fail
+validation, so these run on a host without a GPU.
+"""
+import os
+import re
+
+import pytest
+
+import kv_cache_absorption_attn_amd as ispa
+from kv_cache_absorption_attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ispa.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+A = 0x10000        # fake 16-byte aligned address, never dereferenced
+MIS = 0x10008      # fake misaligned address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ispa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ispa_attn_decomp", "ispa_gram_accumulate", "ispa_ridge_solve",
+              "ispa_ridge_workspace_bytes", "ispa_layer_score", "ispa_apply_dW",
+              "ispa_project", "ispa_status_string", "ispa_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    for n in declared_functions():
+        assert hasattr(_lib.lib, n), n
+    assert set(declared_functions()) == set(_lib.EXPORTED)
+
+
+def test_status_strings():
+    assert ispa.ispa_status_string(0) == "ok"
+    for s in range(1, 7):
+        assert ispa.ispa_status_string(s) not in ("ok", "unknown status")
+    assert ispa.ispa_status_string(99) == "unknown status"
+    assert ispa.ispa_version() >= 100
+
+
+def attn(**kw):
+    args = dict(q=A, n_q=16, ks=A, vs=A, n_sink=8, kc=A, vc=A, n_cur=8, kh=0, vh=0, n_hist=0,
+                heads=2, d=128, scale=0.1, ol=A, ll=0, oh=0, lh=0, of=0, lf=0, do=0, stream=0)
+    args.update(kw)
+    return _lib.lib.ispa_attn_decomp(*args.values())
+
+
+def test_attn_validation():
+    assert attn(q=0) == NULL
+    assert attn(d=96) == UNSUP
+    assert attn(d=32) == UNSUP
+    assert attn(n_sink=0, n_cur=0) == SHAPE
+    assert attn(n_q=-1) == SHAPE
+    assert attn(heads=0) == SHAPE
+    assert attn(scale=0.0) == SHAPE
+    assert attn(scale=float("nan")) == SHAPE
+    assert attn(ol=0) == NULL                      # no output requested
+    assert attn(n_hist=5) == NULL                  # history length without pointers
+    assert attn(ks=0) == NULL
+    assert attn(q=MIS) == ALIGN
+    assert attn(ol=MIS) == ALIGN
+
+
+def test_gram_validation():
+    g = _lib.lib.ispa_gram_accumulate
+    assert g(0, A, 10, 128, 1, A, A, 0, 0, 0) == NULL
+    assert g(A, A, 10, 128, 1, 0, A, 0, 0, 0) == NULL
+    assert g(A, A, 10, 0, 1, A, A, 0, 0, 0) == SHAPE
+    assert g(A, A, -1, 128, 1, A, A, 0, 0, 0) == SHAPE
+    assert g(A, A, 10, 128, 0, A, A, 0, 0, 0) == SHAPE
+    assert g(A, A, 10, 100, 1, A, A, 0, 0, 0) == UNSUP
+    assert g(A, MIS, 10, 128, 1, A, A, 0, 0, 0) == ALIGN
+    assert g(A, A, 0, 128, 1, A, A, 0, 0, 0) == OK     # nothing to add, nothing launched
+
+
+def test_ridge_validation():
+    r = _lib.lib.ispa_ridge_solve
+    need = ispa.ispa_ridge_workspace_bytes(2, 256)
+    assert need > 3 * 2 * 256 * 256 * 4
+    assert ispa.ispa_ridge_workspace_bytes(0, 256) == 0
+    assert ispa.ispa_ridge_workspace_bytes(4, 256) > need
+    assert r(2, 256, 0, A, A, 0.01, A, A, A, need, 0) == NULL
+    assert r(0, 256, A, A, A, 0.01, A, A, A, need, 0) == SHAPE
+    assert r(2, 256, A, A, A, -1.0, A, A, A, need, 0) == SHAPE
+    assert r(2, 256, A, A, A, float("inf"), A, A, A, need, 0) == SHAPE
+    assert r(2, 250, A, A, A, 0.01, A, A, A, need, 0) == UNSUP
+    assert r(2, 256, A, A, A, 0.01, A, A, A, need - 1, 0) == WS
+    assert r(2, 256, A, A, A, 0.01, A, A, 0, need, 0) == WS
+    assert r(2, 256, A, A, MIS, 0.01, A, A, A, need, 0) == ALIGN
+
+
+def test_score_apply_project_validation():
+    s = _lib.lib.ispa_layer_score
+    need = ispa.ispa_ridge_workspace_bytes(2, 256)
+    assert s(2, 256, A, A, 0, A, A, 0.01, A, 1, A, need, A, A, A, 0) == NULL
+    assert s(2, 256, A, A, A, A, A, 0.01, A, -1, A, need, A, A, A, 0) == SHAPE
+    assert s(2, 256, A, A, A, A, A, 0.01, A, 1, A, 16, A, A, A, 0) == WS
+    a = _lib.lib.ispa_apply_dW
+    assert a(2, 256, 0, A, A, 0) == NULL
+    assert a(0, 256, A, A, A, 0) == SHAPE
+    assert a(2, 12, A, A, A, 0) == UNSUP
+    p = _lib.lib.ispa_project
+    assert p(A, A, 0, 4, 128, 128, 0) == NULL
+    assert p(A, A, A, -4, 128, 128, 0) == SHAPE
+    assert p(A, A, A, 4, 100, 128, 0) == UNSUP
+    assert p(A, A, A, 0, 128, 128, 0) == OK
