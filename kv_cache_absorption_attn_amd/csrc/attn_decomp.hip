@@ -25,6 +25,8 @@
 // 2^8 (the result is exact either way; it only bounds p <= 256), which keeps
 // the O rescale off the common path.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "ispa_internal.h"
 
@@ -36,19 +38,16 @@ constexpr int kQTile = 128;
 constexpr int kKTile = 64;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-// LDS position of key `key` (0..63) inside a V^T row: within each group of 16
-// keys, key = 8a + 4h + r goes to 8h + 4a + r.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~15) | ((key & 4) << 1) | ((key & 8) >> 1) | (key & 3);
-}
+// K and V tiles are staged in LDS in their natural [key][d] layout, with
+// direct-to-LDS global loads (each wave instruction writes 64 lanes x 16 bytes
+// contiguously). The 16-byte chunk c of key row r is stored at chunk position
+// c ^ swz(r): consecutive rows spread the same logical chunk over 8 bank
+// groups, which keeps both the 16-byte K fragment reads and the 8-byte
+// transposing V reads free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
-template <int D>
-struct TileRegs {
-  static constexpr int KL = D / 32;  // 16-byte K chunks per thread
-  static constexpr int KPT = D / 32; // V keys per thread
-  uint4 k[KL];
-  uint4 v[KPT];
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define ISPA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
 struct Seg {
   const uint16_t* k;
@@ -56,90 +55,41 @@ struct Seg {
   int64_t n;
 };
 
+// Issue the direct-to-LDS loads of one 64-key tile of K and V into (ks, vs).
+// Rows past `valid` re-load the last valid row (in bounds); their scores are
+// masked to -inf, so they contribute nothing.
 template <int D>
-__device__ __forceinline__ void load_k(TileRegs<D>& r, const Seg& sg, int64_t row0,
-                                       int valid, int64_t rs, int head, int tid) {
-  constexpr int CPR = D / 8;            // 16-byte chunks per key row
-  constexpr int RPP = kThreads / CPR;   // K rows per pass
-  // K: coalesced rows, thread -> (row, chunk)
-  {
-    const int c = tid % CPR, r0 = tid / CPR;
+__device__ __forceinline__ void issue_tile(const Seg& sg, int64_t row0, int valid, int64_t rs,
+                                           int head, uint16_t* ks, uint16_t* vs, int wave,
+                                           int lane) {
+  constexpr int CPR = D / 8;                // 16-byte chunks per key row
+  constexpr int RPI = 64 / CPR;             // rows per wave instruction
+  constexpr int IPW = kKTile / RPI / 4;     // instructions per wave per tensor
+  const int p = lane % CPR;
 #pragma unroll
-    for (int p = 0; p < TileRegs<D>::KL; ++p) {
-      const int row = r0 + p * RPP;
-      if (row < valid) {
-        r.k[p] = *reinterpret_cast<const uint4*>(sg.k + (row0 + row) * rs + head * D + 8 * c);
-      } else {
-        r.k[p] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  for (int i = 0; i < IPW; ++i) {
+    const int r = (wave * IPW + i) * RPI + lane / CPR;
+    const int rr = r < valid ? r : valid - 1;
+    const int c = p ^ swz(r);
+    const int64_t off = (row0 + rr) * rs + head * D + 8 * c;
+    const int lds_off = (wave * IPW + i) * RPI * D;   // elements; lane adds lane*8
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sg.k + off),
+                                     ISPA_LDS(void, ks + lds_off), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sg.v + off),
+                                     ISPA_LDS(void, vs + lds_off), 16, 0, 0);
   }
 }
 
+// 16-byte K fragment: key row r, logical chunk c.
 template <int D>
-__device__ __forceinline__ void load_v(TileRegs<D>& r, const Seg& sg, int64_t row0,
-                                       int valid, int64_t rs, int head, int tid) {
-  // V: thread -> (key group, d chunk); KPT consecutive keys, 8 d values
-  {
-    constexpr int KPT = TileRegs<D>::KPT;
-    constexpr int NG = kKTile / KPT;
-    const int kg = tid % NG, dc = tid / NG;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int row = kg * KPT + j;
-      if (row < valid) {
-        r.v[j] = *reinterpret_cast<const uint4*>(sg.v + (row0 + row) * rs + head * D + 8 * dc);
-      } else {
-        r.v[j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
+__device__ __forceinline__ bf16x8 k_frag(const uint16_t* ks, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * (c ^ swz(r)));
 }
 
+// Address a lane supplies to the transposing read: V[key][d .. d+3].
 template <int D>
-__device__ __forceinline__ void store_k(const TileRegs<D>& r, uint16_t* ks, int tid) {
-  constexpr int KSTR = D + 8;
-  constexpr int CPR = D / 8;
-  constexpr int RPP = kThreads / CPR;
-  const int c = tid % CPR, r0 = tid / CPR;
-#pragma unroll
-  for (int p = 0; p < TileRegs<D>::KL; ++p) {
-    *reinterpret_cast<uint4*>(ks + (r0 + p * RPP) * KSTR + 8 * c) = r.k[p];
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_v(const TileRegs<D>& r, uint16_t* vt, int tid) {
-  constexpr int VSTR = kKTile + 8;
-  {
-    constexpr int KPT = TileRegs<D>::KPT;
-    constexpr int NG = kKTile / KPT;
-    const int kg = tid % NG, dc = tid / NG;
-    const int pos = vt_pos(kg * KPT);
-    const uint32_t* w[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) w[j] = reinterpret_cast<const uint32_t*>(&r.v[j]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t* dst = vt + (8 * dc + e) * VSTR + pos;
-      const int wi = e >> 1;
-      if constexpr (KPT == 4) {
-        uint2 val;
-        if ((e & 1) == 0) {
-          val.x = pack_lo16(w[0][wi], w[1][wi]);
-          val.y = pack_lo16(w[2][wi], w[3][wi]);
-        } else {
-          val.x = pack_hi16(w[0][wi], w[1][wi]);
-          val.y = pack_hi16(w[2][wi], w[3][wi]);
-        }
-        *reinterpret_cast<uint2*>(dst) = val;
-      } else {
-        uint32_t val = (e & 1) == 0 ? pack_lo16(w[0][wi], w[1][wi])
-                                    : pack_hi16(w[0][wi], w[1][wi]);
-        *reinterpret_cast<uint32_t*>(dst) = val;
-      }
-    }
-  }
+__device__ __forceinline__ const uint16_t* v_addr(const uint16_t* vs, int key, int d) {
+  return vs + key * D + 8 * ((d >> 3) ^ swz(key)) + (d & 7);
 }
 
 template <int D>
@@ -175,12 +125,15 @@ __device__ __forceinline__ void store_packed(uint16_t* out, const uint32_t (*o)[
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnParams p) {
-  constexpr int KSTR = D + 8;
-  constexpr int VSTR = kKTile + 8;
-  constexpr int KBUF = kKTile * KSTR;
-  constexpr int VBUF = D * VSTR;
+  constexpr int TBUF = kKTile * D;   // one K or V tile (elements)
   constexpr int NB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KBUF + VBUF)];
+  // Four separate LDS arrays (K and V, two buffers each): every access below
+  // names a fixed array, so the compiler can see that the prefetch into one
+  // buffer never aliases the reads of the other and needs no early wait.
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[TBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[TBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sv0[TBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sv1[TBUF];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, l32 = lane % 32, hf = lane / 32;
@@ -232,51 +185,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
   uint32_t o_loc[NB][8];
   float lse_loc2 = -INFINITY;
 
-  TileRegs<D> regs;
+  // per-lane constants of the transposing V reads: 16-lane group g, index i
+  const int vg = lane / 16, vi = lane % 16;
+  const int v_key = 4 * (vg / 2) + vi / 4;            // + 16 st (+ 8 for slots 4..7)
+  const int v_d = 16 * (vg % 2) + 4 * (vi % 4);       // + 32 db
+
   {
     Seg sg;
     int valid;
     int64_t row0;
     tile_of(0, sg, row0, valid);
-    load_k<D>(regs, sg, row0, valid, rs, head, tid);
-    load_v<D>(regs, sg, row0, valid, rs, head, tid);
-    store_k<D>(regs, smem, tid);
-    store_v<D>(regs, smem + 2 * KBUF, tid);
+    issue_tile<D>(sg, row0, valid, rs, head, sk0, sv0, wave, lane);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int idx = 0; idx < T; ++idx) {
-    const int buf = idx & 1;
-    const uint16_t* ks = smem + buf * KBUF;
-    const uint16_t* vt = smem + 2 * KBUF + buf * VBUF;
+  // One tile; BUF (compile time) selects the LDS buffers it reads, the
+  // prefetch of the next tile goes to the other pair.
+  auto tile_step = [&](auto buf_c, int idx) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const uint16_t* ks = BUF ? sk1 : sk0;
+    const uint16_t* vs = BUF ? sv1 : sv0;
+    uint16_t* nks = BUF ? sk0 : sk1;
+    uint16_t* nvs = BUF ? sv0 : sv1;
     Seg sg;
     int valid;
     int64_t row0;
     tile_of(idx, sg, row0, valid);
     const bool has_next = idx + 1 < T;
-    Seg s2 = sg;
-    int v2 = 0;
-    int64_t r2 = 0;
     if (has_next) {
+      Seg s2;
+      int v2;
+      int64_t r2;
       tile_of(idx + 1, s2, r2, v2);
-      load_k<D>(regs, s2, r2, v2, rs, head, tid);
+      issue_tile<D>(s2, r2, v2, rs, head, nks, nvs, wave, lane);
     }
 
     // S^T = K Q^T
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ks + l32 * KSTR + 16 * t + 8 * hf);
-      const bf16x8 a1 =
-          *reinterpret_cast<const bf16x8*>(ks + (32 + l32) * KSTR + 16 * t + 8 * hf);
+      const bf16x8 a0 = k_frag<D>(ks, l32, 2 * t + hf);
+      const bf16x8 a1 = k_frag<D>(ks, 32 + l32, 2 * t + hf);
       s0 = mfma32x32x16(a0, qf[t], s0);
       s1 = mfma32x32x16(a1, qf[t], s1);
     }
 
-    if (has_next) {
-      store_k<D>(regs, smem + (buf ^ 1) * KBUF, tid);
-      load_v<D>(regs, s2, r2, v2, rs, head, tid);
-    }
 
     if (valid < kKTile) {
 #pragma unroll
@@ -304,6 +258,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
       for (int b = 0; b < NB; ++b) oacc[b] *= alpha;
     }
 
+    // P = 2^(s * scale_log2 - m); the row sum is kept in fp32 (the LSE needs
+    // it), P goes to the PV product rounded to bf16.
     bf16x8 pf[4];
     float lsum = 0.f;
 #pragma unroll
@@ -321,13 +277,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
     for (int db = 0; db < NB; ++db) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(vt + (32 * db + l32) * VSTR + 16 * st + 8 * hf);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            ISPA_LDS(s16x4, v_addr<D>(vs, 16 * st + v_key, 32 * db + v_d)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            ISPA_LDS(s16x4, v_addr<D>(vs, 16 * st + 8 + v_key, 32 * db + v_d)));
+        const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
+                                                 __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3,
+                                                 4, 5, 6, 7);
         oacc[db] = mfma32x32x16(a, pf[st], oacc[db]);
       }
     }
 
-    if (has_next) store_v<D>(regs, smem + 2 * KBUF + (buf ^ 1) * VBUF, tid);
 
     if (split && idx == n_local_tiles - 1) {
       const float lt = l_run + __shfl_xor(l_run, 32);
@@ -348,7 +308,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
 #pragma unroll
       for (int b = 0; b < NB; ++b) oacc[b] = f32x16{};
     }
+    // the next tile's direct-to-LDS loads (issued at the top) must land
+    // before any wave reads them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  for (int idx = 0; idx < T; idx += 2) {
+    tile_step(std::integral_constant<int, 0>{}, idx);
+    if (idx + 1 < T) tile_step(std::integral_constant<int, 1>{}, idx + 1);
   }
 
   if (!qvalid) return;
