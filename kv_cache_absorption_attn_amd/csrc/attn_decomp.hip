@@ -41,10 +41,15 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units
 // K and V tiles are staged in LDS in their natural [key][d] layout, with
 // direct-to-LDS global loads (each wave instruction writes 64 lanes x 16 bytes
 // contiguously). The 16-byte chunk c of key row r is stored at chunk position
-// c ^ swz(r): consecutive rows spread the same logical chunk over 8 bank
-// groups, which keeps both the 16-byte K fragment reads and the 8-byte
-// transposing V reads free of bank conflicts.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// c ^ swz(r). With the 64-bank LDS this keeps both access patterns free of
+// bank conflicts: 16 consecutive rows read the same logical chunk (K
+// fragments, 16 lanes per pass) and 4 consecutive rows x 4 adjacent chunks
+// (transposing V reads, 32 lanes per pass).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return ((r & 2) << 1) | ((r >> 2) & 3);
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define ISPA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
@@ -55,41 +60,70 @@ struct Seg {
   int64_t n;
 };
 
-// Issue the direct-to-LDS loads of one 64-key tile of K and V into (ks, vs).
-// Rows past `valid` re-load the last valid row (in bounds); their scores are
-// masked to -inf, so they contribute nothing.
+// Direct-to-LDS loads of one 64-key tile of K and V. Each lane's byte offset
+// inside a full tile is fixed, so a full tile only moves a uniform base.
+// In a tail tile, rows past `valid` re-load the last valid row (in bounds);
+// their scores are masked to -inf, so they contribute nothing.
 template <int D>
-__device__ __forceinline__ void issue_tile(const Seg& sg, int64_t row0, int valid, int64_t rs,
-                                           int head, uint16_t* ks, uint16_t* vs, int wave,
-                                           int lane) {
-  constexpr int CPR = D / 8;                // 16-byte chunks per key row
-  constexpr int RPI = 64 / CPR;             // rows per wave instruction
-  constexpr int IPW = kKTile / RPI / 4;     // instructions per wave per tensor
-  const int p = lane % CPR;
+struct TileLoader {
+  static constexpr int CPR = D / 8;            // 16-byte chunks per key row
+  static constexpr int RPI = 64 / CPR;         // rows per wave instruction
+  static constexpr int IPW = kKTile / RPI / 4; // instructions per wave per tensor
+  uint32_t off[IPW];                           // bytes, full tile
+  int row[IPW];
+  int chunk_off;                               // head * D (elements)
+  int lds_base;                                // elements
+
+  __device__ void init(int64_t rs, int head, int wave, int lane) {
+    const int p = lane % CPR;
+    chunk_off = head * D;
+    lds_base = wave * IPW * RPI * D;
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int r = (wave * IPW + i) * RPI + lane / CPR;
-    const int rr = r < valid ? r : valid - 1;
-    const int c = p ^ swz(r);
-    const int64_t off = (row0 + rr) * rs + head * D + 8 * c;
-    const int lds_off = (wave * IPW + i) * RPI * D;   // elements; lane adds lane*8
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sg.k + off),
-                                     ISPA_LDS(void, ks + lds_off), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sg.v + off),
-                                     ISPA_LDS(void, vs + lds_off), 16, 0, 0);
+    for (int i = 0; i < IPW; ++i) {
+      row[i] = (wave * IPW + i) * RPI + lane / CPR;
+      const int c = p ^ swz<D>(row[i]);
+      off[i] = static_cast<uint32_t>((row[i] * rs + head * D + 8 * c) * 2);
+    }
   }
-}
+
+  __device__ void issue(const Seg& sg, int64_t row0, int valid, int64_t rs, uint16_t* ks,
+                        uint16_t* vs, int lane) const {
+    const char* kb = reinterpret_cast<const char*>(sg.k + row0 * rs);
+    const char* vb = reinterpret_cast<const char*>(sg.v + row0 * rs);
+    if (valid == kKTile) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        __builtin_amdgcn_global_load_lds(kb + off[i], ISPA_LDS(void, ks + lds_base + i * RPI * D),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + off[i], ISPA_LDS(void, vs + lds_base + i * RPI * D),
+                                         16, 0, 0);
+      }
+    } else {
+      const int p = lane % CPR;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int rr = row[i] < valid ? row[i] : valid - 1;
+        const int c = p ^ swz<D>(row[i]);
+        const int64_t o = (rr * rs + chunk_off + 8 * c) * 2;
+        __builtin_amdgcn_global_load_lds(kb + o, ISPA_LDS(void, ks + lds_base + i * RPI * D), 16,
+                                         0, 0);
+        __builtin_amdgcn_global_load_lds(vb + o, ISPA_LDS(void, vs + lds_base + i * RPI * D), 16,
+                                         0, 0);
+      }
+    }
+  }
+};
 
 // 16-byte K fragment: key row r, logical chunk c.
 template <int D>
 __device__ __forceinline__ bf16x8 k_frag(const uint16_t* ks, int r, int c) {
-  return *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * (c ^ swz(r)));
+  return *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * (c ^ swz<D>(r)));
 }
 
 // Address a lane supplies to the transposing read: V[key][d .. d+3].
 template <int D>
 __device__ __forceinline__ const uint16_t* v_addr(const uint16_t* vs, int key, int d) {
-  return vs + key * D + 8 * ((d >> 3) ^ swz(key)) + (d & 7);
+  return vs + key * D + 8 * ((d >> 3) ^ swz<D>(key)) + (d & 7);
 }
 
 template <int D>
@@ -190,12 +224,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
   const int v_key = 4 * (vg / 2) + vi / 4;            // + 16 st (+ 8 for slots 4..7)
   const int v_d = 16 * (vg % 2) + 4 * (vi % 4);       // + 32 db
 
+  TileLoader<D> loader;
+  loader.init(rs, head, wave, lane);
   {
     Seg sg;
     int valid;
     int64_t row0;
     tile_of(0, sg, row0, valid);
-    issue_tile<D>(sg, row0, valid, rs, head, sk0, sv0, wave, lane);
+    loader.issue(sg, row0, valid, rs, sk0, sv0, lane);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -218,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
       int v2;
       int64_t r2;
       tile_of(idx + 1, s2, r2, v2);
-      issue_tile<D>(s2, r2, v2, rs, head, nks, nvs, wave, lane);
+      loader.issue(s2, r2, v2, rs, nks, nvs, lane);
     }
 
     // S^T = K Q^T
@@ -233,6 +269,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
 
 
     if (valid < kKTile) {
+      // tail tile only: keep this a real branch (the empty volatile asm stops
+      // it from being flattened into unconditional selects)
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = 8 * (i / 4) + 4 * hf + (i % 4);
