@@ -86,6 +86,28 @@ struct TileLoader {
     }
   }
 
+  // one tensor (K or V) of a tile
+  __device__ void issue_one(const uint16_t* src, int64_t row0, int valid, int64_t rs,
+                            uint16_t* dst, int lane) const {
+    const char* b = reinterpret_cast<const char*>(src + row0 * rs);
+    if (valid == kKTile) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_global_load_lds(b + off[i], ISPA_LDS(void, dst + lds_base + i * RPI * D),
+                                         16, 0, 0);
+    } else {
+      const int p = lane % CPR;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int rr = row[i] < valid ? row[i] : valid - 1;
+        const int c = p ^ swz<D>(row[i]);
+        const int64_t o = (rr * rs + chunk_off + 8 * c) * 2;
+        __builtin_amdgcn_global_load_lds(b + o, ISPA_LDS(void, dst + lds_base + i * RPI * D), 16,
+                                         0, 0);
+      }
+    }
+  }
+
   __device__ void issue(const Seg& sg, int64_t row0, int valid, int64_t rs, uint16_t* ks,
                         uint16_t* vs, int lane) const {
     const char* kb = reinterpret_cast<const char*>(sg.k + row0 * rs);
@@ -267,7 +289,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
       s1 = mfma32x32x16(a1, qf[t], s1);
     }
 
-
     if (valid < kKTile) {
       // tail tile only: keep this a real branch (the empty volatile asm stops
       // it from being flattened into unconditional selects)
@@ -311,11 +332,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
     }
     l_run += lsum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T, key step outer so consecutive MFMAs feed independent
+    // accumulators
 #pragma unroll
-    for (int db = 0; db < NB; ++db) {
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int db = 0; db < NB; ++db) {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             ISPA_LDS(s16x4, v_addr<D>(vs, 16 * st + v_key, 32 * db + v_d)));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -409,19 +431,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
   if (p.lse_full && hf == 0) p.lse_full[head * p.n_q + qi] = lse_f2 * kLn2;
 }
 
+
 }  // namespace
 
-hipError_t launch_attn_decomp(const AttnParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_attn_decomp(AttnParams p, int head_dim, hipStream_t stream) {
+  p.n_qtiles = static_cast<int>((p.n_q + kQTile - 1) / kQTile);
   const int blocks = p.n_qtiles * p.n_heads;
   if (blocks == 0) return hipSuccess;
-  if (head_dim == 128) {
+  if (head_dim == 128)
     hipLaunchKernelGGL(attn_decomp_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream, p);
-  } else {
+  else
     hipLaunchKernelGGL(attn_decomp_kernel<64>, dim3(blocks), dim3(kThreads), 0, stream, p);
-  }
   return hipGetLastError();
 }
 
-int attn_q_tile() { return kQTile; }
+int attn_q_tile_min() { return kQTile; }
 
 }  // namespace ispa

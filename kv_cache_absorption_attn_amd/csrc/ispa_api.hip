@@ -103,7 +103,7 @@ int ispa_attn_decomp(const void* q, int64_t n_q, const void* k_sink, const void*
                         o_hist, lse_hist, o_full, lse_full, d_out};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return ISPA_ERR_ALIGN;
-  const int64_t qtiles = (n_q + ispa::attn_q_tile() - 1) / ispa::attn_q_tile();
+  const int64_t qtiles = (n_q + ispa::attn_q_tile_min() - 1) / ispa::attn_q_tile_min();
   if (qtiles * n_heads > INT32_MAX) return ISPA_ERR_SHAPE;
   if (n_q == 0) return ISPA_OK;
 
@@ -128,7 +128,6 @@ int ispa_attn_decomp(const void* q, int64_t n_q, const void* k_sink, const void*
   p.o_full = static_cast<uint16_t*>(o_full);
   p.lse_full = lse_full;
   p.d_out = static_cast<uint16_t*>(d_out);
-  p.n_qtiles = static_cast<int>(qtiles);
   const bool only_full = !o_local && !lse_local && !o_hist && !lse_hist && !d_out;
   p.mode = only_full ? 1 : 0;
   p.need_hist = (o_hist || lse_hist || o_full || lse_full || d_out) ? 1 : 0;

@@ -26,8 +26,9 @@ struct AttnParams {
   int mode;                  // 0: local / history split + merge; 1: one pass (full only)
   int need_hist;             // split mode: history phase and merge needed
 };
-hipError_t launch_attn_decomp(const AttnParams& p, int head_dim, hipStream_t stream);
-int attn_q_tile();
+// Fills p.n_qtiles, then launches.
+hipError_t launch_attn_decomp(AttnParams p, int head_dim, hipStream_t stream);
+int attn_q_tile_min();  // smallest query tile of any attention kernel
 
 // ---------------------------------------------------------------- Gram
 struct GramParams {
