@@ -40,19 +40,10 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 // K and V tiles are staged in LDS in their natural [key][d] layout, with
 // direct-to-LDS global loads (each wave instruction writes 64 lanes x 16 bytes
-// contiguously). The 16-byte chunk c of key row r is stored at chunk position
-// c ^ swz(r). With the 64-bank LDS this keeps both access patterns free of
-// bank conflicts: 16 consecutive rows read the same logical chunk (K
-// fragments, 16 lanes per pass) and 4 consecutive rows x 4 adjacent chunks
-// (transposing V reads, 32 lanes per pass).
+// contiguously), swizzled by lds_swz so that both the 16-byte K fragment
+// reads and the transposing V reads are free of bank conflicts.
 template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return ((r & 2) << 1) | ((r >> 2) & 3);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define ISPA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+__device__ __forceinline__ int swz(int r) { return lds_swz<D>(r); }
 
 struct Seg {
   const uint16_t* k;
@@ -83,28 +74,6 @@ struct TileLoader {
       row[i] = (wave * IPW + i) * RPI + lane / CPR;
       const int c = p ^ swz<D>(row[i]);
       off[i] = static_cast<uint32_t>((row[i] * rs + head * D + 8 * c) * 2);
-    }
-  }
-
-  // one tensor (K or V) of a tile
-  __device__ void issue_one(const uint16_t* src, int64_t row0, int valid, int64_t rs,
-                            uint16_t* dst, int lane) const {
-    const char* b = reinterpret_cast<const char*>(src + row0 * rs);
-    if (valid == kKTile) {
-#pragma unroll
-      for (int i = 0; i < IPW; ++i)
-        __builtin_amdgcn_global_load_lds(b + off[i], ISPA_LDS(void, dst + lds_base + i * RPI * D),
-                                         16, 0, 0);
-    } else {
-      const int p = lane % CPR;
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int rr = row[i] < valid ? row[i] : valid - 1;
-        const int c = p ^ swz<D>(row[i]);
-        const int64_t o = (rr * rs + chunk_off + 8 * c) * 2;
-        __builtin_amdgcn_global_load_lds(b + o, ISPA_LDS(void, dst + lds_base + i * RPI * D), 16,
-                                         0, 0);
-      }
     }
   }
 
@@ -140,12 +109,6 @@ struct TileLoader {
 template <int D>
 __device__ __forceinline__ bf16x8 k_frag(const uint16_t* ks, int r, int c) {
   return *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * (c ^ swz<D>(r)));
-}
-
-// Address a lane supplies to the transposing read: V[key][d .. d+3].
-template <int D>
-__device__ __forceinline__ const uint16_t* v_addr(const uint16_t* vs, int key, int d) {
-  return vs + key * D + 8 * ((d >> 3) ^ swz<D>(key)) + (d & 7);
 }
 
 template <int D>
@@ -241,10 +204,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
   uint32_t o_loc[NB][8];
   float lse_loc2 = -INFINITY;
 
-  // per-lane constants of the transposing V reads: 16-lane group g, index i
-  const int vg = lane / 16, vi = lane % 16;
-  const int v_key = 4 * (vg / 2) + vi / 4;            // + 16 st (+ 8 for slots 4..7)
-  const int v_d = 16 * (vg % 2) + 4 * (vi % 4);       // + 32 db
 
   TileLoader<D> loader;
   loader.init(rs, head, wave, lane);
@@ -338,13 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnPara
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int db = 0; db < NB; ++db) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            ISPA_LDS(s16x4, v_addr<D>(vs, 16 * st + v_key, 32 * db + v_d)));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            ISPA_LDS(s16x4, v_addr<D>(vs, 16 * st + 8 + v_key, 32 * db + v_d)));
-        const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
-                                                 __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3,
-                                                 4, 5, 6, 7);
+        const bf16x8 a = tr_operand<D>(vs, 16 * st, 32 * db, lane);
         oacc[db] = mfma32x32x16(a, pf[st], oacc[db]);
       }
     }

@@ -53,6 +53,46 @@ __device__ __forceinline__ f32x16 mfma32x32x2f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// LDS tiles of 16-bit elements with rows of D elements (D = 128: 256-byte
+// rows; D = 64: 128-byte rows) store the 16-byte chunk c of row r at chunk
+// position c ^ lds_swz<D>(r). With the 64-bank LDS this spreads 16
+// consecutive rows reading one logical chunk (16-byte operand reads, 16 lanes
+// per pass) and 4 consecutive rows x 4 adjacent chunks (transposing 8-byte
+// reads, 32 lanes per pass) over distinct banks.
+template <int D>
+__device__ __forceinline__ int lds_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return ((r & 2) << 1) | ((r >> 2) & 3);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define ISPA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+
+// Element (row, col) of a swizzled LDS tile with rows of D elements.
+template <int D>
+__device__ __forceinline__ const uint16_t* swz_addr(const uint16_t* base, int row, int col) {
+  return base + row * D + 8 * ((col >> 3) ^ lds_swz<D>(row)) + (col & 7);
+}
+
+// MFMA operand whose contraction index runs along the rows of a swizzled
+// LDS tile (rows = contraction index, columns = the operand's m or n index):
+// lane l receives the 8 elements (rows r(j), column col0 + l%32), j = 0..7,
+// with r(j) = row0 + 8*(j/4) + 4*(l/32) + (j%4), by two transposing reads
+// (ds_read_b64_tr_b16: within each 16-lane group, lane i gets element i%4 of
+// the rows supplied by lanes i/4, i/4+4, i/4+8, i/4+12).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* base, int row0, int col0, int lane) {
+  const int g = lane / 16, i = lane % 16;
+  const int r = row0 + 4 * (g / 2) + i / 4;
+  const int c = col0 + 16 * (g % 2) + 4 * (i % 4);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS(s16x4, swz_addr<D>(base, r, c)));
+  const s16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS(s16x4, swz_addr<D>(base, r + 8, c)));
+  typedef __bf16 bf16x4_local __attribute__((ext_vector_type(4)));
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4_local, lo),
+                                 __builtin_bit_cast(bf16x4_local, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X. Remap
 // the hardware block id so that consecutive logical work items land on the
 // same XCD (and share its L2): logical id = start(xcd) + bid / 8.

@@ -22,51 +22,53 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kT = 128;          // output tile edge
 constexpr int kTok = 64;         // tokens per LDS stage
-constexpr int kTStr = kTok + 8;  // LDS row stride (bf16) of a Y^T tile
+constexpr int kBuf = kTok * kT;  // elements of one operand stage (16 KB)
 
-// One operand of the Gram: a 128-feature block of Y staged as Y^T[f][t].
-// Thread -> (token group of 4, 8-feature chunk): 4 row loads of 16 bytes,
-// written as 8 transposed 8-byte chunks.
+// Direct-to-LDS loads of one stage of a 128-feature block of Y (token-major
+// rows of 256 bytes, swizzled as lds_swz<128>). Each wave instruction writes
+// 4 rows. Features past the block's end are clamped to a valid column (they
+// only feed outputs that are never stored); tokens past n_tok are clamped
+// here and zeroed in LDS afterwards.
 struct GramLoader {
-  uint4 r[4];
-  __device__ void load(const uint16_t* base, int h, int fvalid, int64_t t0, int64_t n_tok,
-                       int tid) {
-    const int tg = tid % 16, fc = tid / 16;
+  int row[4];
+  int col[4];   // element offset of the lane's 16-byte chunk within the block
+  __device__ void init(int wave, int lane, int fvalid) {
+    const int p = lane % 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t t = t0 + 4 * tg + j;
-      if (t < n_tok && 8 * fc < fvalid) {
-        r[j] = *reinterpret_cast<const uint4*>(base + t * h + 8 * fc);
-      } else {
-        r[j] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < 4; ++i) {
+      row[i] = (wave * 4 + i) * 4 + lane / 16;
+      int c = p ^ lds_swz<kT>(row[i]);
+      if (8 * c >= fvalid) c = fvalid / 8 - 1;
+      col[i] = 8 * c;
     }
   }
-  __device__ void store(uint16_t* S, int tid) const {
-    const int tg = tid % 16, fc = tid / 16;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
+  __device__ void issue(const uint16_t* src, int h, int64_t t0, int64_t n_tok,
+                        uint16_t* dst, int wave) const {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int wi = e >> 1;
-      uint2 v;
-      if ((e & 1) == 0) {
-        v.x = pack_lo16(w0[wi], w1[wi]);
-        v.y = pack_lo16(w2[wi], w3[wi]);
-      } else {
-        v.x = pack_hi16(w0[wi], w1[wi]);
-        v.y = pack_hi16(w2[wi], w3[wi]);
-      }
-      *reinterpret_cast<uint2*>(S + (8 * fc + e) * kTStr + 4 * tg) = v;
+    for (int i = 0; i < 4; ++i) {
+      int64_t t = t0 + row[i];
+      if (t >= n_tok) t = n_tok - 1;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + t * h + col[i]),
+                                       ISPA_LDS(void, dst + (wave * 4 + i) * 4 * kT), 16, 0, 0);
     }
   }
 };
 
+// Zero rows [valid, kTok) of a stage buffer (tail stage only).
+__device__ __forceinline__ void zero_rows(uint16_t* buf, int valid, int tid) {
+  for (int e = valid * (kT / 8) + tid; e < kTok * (kT / 8); e += kThreads)
+    *reinterpret_cast<uint4*>(buf + 8 * e) = make_uint4(0, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, int nbp,
                                                             int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][kT * kTStr];
+  // 4 operand stages (A0 A1 B0 B1, 16 KB each); after the contraction the
+  // same 64 KB (+ padding) holds the fp32 output tile for the epilogue.
+  __shared__ __attribute__((aligned(16))) uint16_t stage_buf[4 * kBuf + 2 * 4 * kT];
+  uint16_t* sa0 = stage_buf;
+  uint16_t* sa1 = stage_buf + kBuf;
+  uint16_t* sb0 = stage_buf + 2 * kBuf;
+  uint16_t* sb1 = stage_buf + 3 * kBuf;
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, l32 = lane % 32, hf = lane / 32;
@@ -100,6 +102,8 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
   if (dest == nullptr) return;
 
   GramLoader li, lj;
+  li.init(wave, lane, fvi);
+  lj.init(wave, lane, fvj);
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -107,84 +111,105 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int nst = static_cast<int>((p.n_tok + kTok - 1) / kTok);
+  const int tail = static_cast<int>(p.n_tok - static_cast<int64_t>(nst - 1) * kTok);
   if (nst > 0) {
-    li.load(srci, h, fvi, 0, p.n_tok, tid);
-    lj.load(srcj, h, fvj, 0, p.n_tok, tid);
-    li.store(smem[0][0], tid);
-    lj.store(smem[0][1], tid);
+    li.issue(srci, h, 0, p.n_tok, sa0, wave);
+    lj.issue(srcj, h, 0, p.n_tok, sb0, wave);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (nst == 1 && tail < kTok) {
+      zero_rows(sa0, tail, tid);
+      zero_rows(sb0, tail, tid);
+      __syncthreads();
+    }
   }
-  __syncthreads();
 
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
+  // One stage: contract 64 tokens of the buffers (ra, rb) while the next
+  // stage lands in (na, nb). Restrict pointers: the buffer being filled never
+  // aliases the ones being read, so the reads need not wait for the loads.
+  auto stage = [&](int s, const uint16_t* __restrict__ ra, const uint16_t* __restrict__ rb,
+                   uint16_t* __restrict__ na, uint16_t* __restrict__ nb) {
     const bool has_next = s + 1 < nst;
     if (has_next) {
-      li.load(srci, h, fvi, static_cast<int64_t>(s + 1) * kTok, p.n_tok, tid);
-      lj.load(srcj, h, fvj, static_cast<int64_t>(s + 1) * kTok, p.n_tok, tid);
+      li.issue(srci, h, static_cast<int64_t>(s + 1) * kTok, p.n_tok, na, wave);
+      lj.issue(srcj, h, static_cast<int64_t>(s + 1) * kTok, p.n_tok, nb, wave);
     }
-    const uint16_t* si = smem[buf][0];
-    const uint16_t* sj = smem[buf][1];
 #pragma unroll
-    for (int kk = 0; kk < kTok / 16; ++kk) {
-      bf16x8 a[2], bb[2];
+    for (int st = 0; st < kTok / 16; ++st) {
+      bf16x8 a[2], bv[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(si + (wm * 64 + i * 32 + l32) * kTStr +
-                                                16 * kk + 8 * hf);
+      for (int i = 0; i < 2; ++i) a[i] = tr_operand<kT>(ra, 16 * st, wm * 64 + i * 32, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bb[j] = *reinterpret_cast<const bf16x8*>(sj + (wn * 64 + j * 32 + l32) * kTStr +
-                                                 16 * kk + 8 * hf);
+      for (int j = 0; j < 2; ++j) bv[j] = tr_operand<kT>(rb, 16 * st, wn * 64 + j * 32, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], bb[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], bv[j], acc[i][j]);
     }
-    if (has_next) {
-      li.store(smem[buf ^ 1][0], tid);
-      lj.store(smem[buf ^ 1][1], tid);
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (has_next && s + 2 == nst && tail < kTok) {
+      zero_rows(na, tail, tid);
+      zero_rows(nb, tail, tid);
+      __syncthreads();
+    }
+  };
+  for (int s = 0; s < nst; ++s) {
+    const bool odd = s & 1;
+    stage(s, odd ? sa1 : sa0, odd ? sb1 : sb0, odd ? sa0 : sa1, odd ? sb0 : sb1);
   }
 
-  // dest(fi0 + m, fj0 + n) (+)= acc; mirror tile for off-diagonal G / E tiles.
-  const bool mirror = (i_is_d == j_is_d) && bi != bj;
+  // Epilogue through LDS: the finished 128 x 128 fp32 tile is staged in the
+  // (now idle) operand buffers, then added to dest(fi0 + m, fj0 + n) with
+  // row-contiguous float4 accesses, and - for off-diagonal G / E tiles - to
+  // the mirror tile dest(fj0 + n, fi0 + m), read back transposed.
+  constexpr int kLd = kT + 4;   // fp32 row stride of the staged tile
+  float* st = reinterpret_cast<float*>(stage_buf);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = wn * 64 + j * 32 + l32;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int m0 = wm * 64 + i * 32 + 8 * g + 4 * hf;
-        if (n < fvj) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (m0 + r < fvi) {
-              float* c = dest + static_cast<int64_t>(fi0 + m0 + r) * h + fj0 + n;
-              const float v = acc[i][j][4 * g + r];
-              *c = p.zero_first ? v : *c + v;
-            }
-          }
-          if (mirror && m0 + 4 <= fvi) {
-            float4* c = reinterpret_cast<float4*>(dest + static_cast<int64_t>(fj0 + n) * h +
-                                                  fi0 + m0);
-            float4 v = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                   acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-            if (!p.zero_first) {
-              const float4 o = *c;
-              v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-            }
-            *c = v;
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * 64 + i * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+        st[m * kLd + n] = acc[i][j][r];
       }
+    }
+  __syncthreads();
+  const bool mirror = (i_is_d == j_is_d) && bi != bj;
+  // direct tile: thread -> (row m, 4 columns); 32 float4 per row
+  for (int e = tid; e < kT * (kT / 4); e += kThreads) {
+    const int m = e / (kT / 4), n4 = (e % (kT / 4)) * 4;
+    if (m >= fvi || n4 >= fvj) continue;
+    const float* sv = st + m * kLd + n4;
+    float4 v = make_float4(sv[0], sv[1], sv[2], sv[3]);
+    float4* c = reinterpret_cast<float4*>(dest + static_cast<int64_t>(fi0 + m) * h + fj0 + n4);
+    if (!p.zero_first) {
+      const float4 o = *c;
+      v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+    }
+    *c = v;
+  }
+  if (mirror) {
+    // mirror tile: thread -> (row n, 4 columns m)
+    for (int e = tid; e < kT * (kT / 4); e += kThreads) {
+      const int n = e / (kT / 4), m4 = (e % (kT / 4)) * 4;
+      if (n >= fvj || m4 >= fvi) continue;
+      float4 v = make_float4(st[m4 * kLd + n], st[(m4 + 1) * kLd + n], st[(m4 + 2) * kLd + n],
+                             st[(m4 + 3) * kLd + n]);
+      float4* c = reinterpret_cast<float4*>(dest + static_cast<int64_t>(fj0 + n) * h + fi0 + m4);
+      if (!p.zero_first) {
+        const float4 o = *c;
+        v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+      }
+      *c = v;
     }
   }
 }
 
 // ---------------------------------------------------------------- projection
-constexpr int kPK = 32;           // k per stage
+constexpr int kPK = 32;           // k per stage (projection)
 constexpr int kPStr = kPK + 8;    // LDS row stride (bf16)
 
 __global__ __launch_bounds__(kThreads, 2) void project_kernel(const uint16_t* __restrict__ x,
