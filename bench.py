@@ -16,6 +16,8 @@ measured with HIP events around the attention launches of the timed steps.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
@@ -32,6 +34,20 @@ import workloads as wl  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
+METRIC = "decomp-attention TFLOP/s (% bf16 MFMA peak) + \u0394W absorb ms/layer, 14B-class"
+
+# HBM traffic of the attention and Gram kernels, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, WRITE_SIZE) of this script, written by --pmc-summary. The
+# figures are used only while the kernel sources still hash to the recorded
+# value; otherwise `traffic` is null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_gram_wan14b_warmup_hbm_traffic.md")
+KERNEL_SOURCES = {
+    "attn_decomp_kernel<128>": ["kv_cache_absorption_attn_amd/csrc/attn_decomp.hip",
+                                "kv_cache_absorption_attn_amd/csrc/device_common.h"],
+    "gram_kernel": ["kv_cache_absorption_attn_amd/csrc/gram.hip",
+                    "kv_cache_absorption_attn_amd/csrc/device_common.h"],
+}
+COPY_BYTES = 1 << 30
 
 
 def attn_flops(n_q, n_kv, hidden):
@@ -81,6 +97,7 @@ class Inputs:
         self.o_full = torch.empty(w.n_q, h, dtype=bf, device=dev)
         self.x = torch.empty(w.n_q, h, dtype=bf, device=dev)
         self.dd = torch.empty(w.n_q, h, dtype=bf, device=dev)
+        self.y = torch.empty(w.n_q, h, dtype=bf, device=dev)
         f32 = torch.float32
         self.G = torch.empty(w.n_layers, h, h, dtype=f32, device=dev)
         self.C = torch.empty_like(self.G)
@@ -130,12 +147,30 @@ def run_step(ispa, inp: Inputs, ws, timing: dict | None):
     mark("score1")
     ispa.ispa_apply_dW(inp.selected, inp.dW, inp.wo)
     mark("absorb1")
+    # The first chunk after absorption, at the last warmup history: selected
+    # layers (L-layers) attend their local KV only and project through the
+    # updated W_o; the others (F-layers) run full attention, O_F only, and
+    # project through their own W_o. Which layers are L is a host decision
+    # (their history KV is freed), hence the one read of `selected` here.
+    sel = inp.selected.cpu().tolist()
+    s = w.n_steps - 1
+    mark("post0")
+    for l in range(w.n_layers):
+        if sel[l]:
+            ispa.ispa_attn_decomp(inp.q[l][s], inp.k_sink[l], inp.v_sink[l], inp.k_cur[l][s],
+                                  inp.v_cur[l][s], None, None, w.sm_scale, o_local=inp.x)
+        else:
+            kh, vh = inp.hist_view(l, s)
+            ispa.ispa_attn_decomp(inp.q[l][s], inp.k_sink[l], inp.v_sink[l], inp.k_cur[l][s],
+                                  inp.v_cur[l][s], kh, vh, w.sm_scale, o_full=inp.x)
+        ispa.ispa_project(inp.x, inp.wo[l], inp.y)
+    mark("post1")
     if timing is not None:
         timing.setdefault("events", []).append(ev)
 
 
 def summarize_events(timing):
-    tot = {"attn": 0.0, "gram": 0.0, "ridge": 0.0, "score": 0.0, "apply": 0.0}
+    tot = {"attn": 0.0, "gram": 0.0, "ridge": 0.0, "score": 0.0, "apply": 0.0, "post": 0.0}
     n_attn = 0
     for ev in timing["events"]:
         prev = None
@@ -144,12 +179,227 @@ def summarize_events(timing):
                 dt = prev[1].elapsed_time(e)
                 key = {("attn0", "attn1"): "attn", ("attn1", "gram1"): "gram",
                        ("absorb0", "ridge1"): "ridge", ("ridge1", "score1"): "score",
-                       ("score1", "absorb1"): "apply"}.get((prev[0], tag))
+                       ("score1", "absorb1"): "apply", ("post0", "post1"): "post"
+                       }.get((prev[0], tag))
                 if key:
                     tot[key] += dt
                     n_attn += key == "attn"
             prev = (tag, e)
     return tot, n_attn
+
+
+def stream_measure(ispa, w: wl.Workload, frames=(60, 120), reps: int = 2, seed: int = 1):
+    """Long-horizon streaming after absorption (14B-class): per-chunk time of
+    the attention + output projection of all layers, for the ISPA split
+    (k_select L-layers on local KV, the rest full) against every layer full,
+    at history lengths of `frames` latent frames. The history KV of every
+    layer is resident (the all-full run needs it); the KV bytes reported for
+    ISPA count what its layers keep."""
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    nh, d, h = w.n_heads, w.head_dim, w.hidden
+    tok_per_frame = w.n_cur // 3
+    hmax = tok_per_frame * max(frames)
+
+    def rnd(*shape):
+        return (torch.randn(*shape, generator=g, device=dev) * w.qkv_std).to(bf)
+
+    L = w.n_layers
+    q = [rnd(w.n_q, nh, d) for _ in range(L)]
+    ks = [rnd(w.n_sink, nh, d) for _ in range(L)]
+    vs = [rnd(w.n_sink, nh, d) for _ in range(L)]
+    kc = [rnd(w.n_cur, nh, d) for _ in range(L)]
+    vc = [rnd(w.n_cur, nh, d) for _ in range(L)]
+    kh = [rnd(hmax, nh, d) for _ in range(L)]
+    vh = [rnd(hmax, nh, d) for _ in range(L)]
+    wo = rnd(L, h, h)
+    x = torch.empty(w.n_q, h, dtype=bf, device=dev)
+    y = torch.empty_like(x)
+    is_l = [l % 2 == 0 for l in range(L)]  # every other layer is an L-layer
+    assert sum(is_l) == w.k_select
+    kv_tok_bytes = nh * d * 2 * 2
+
+    def chunk(n_hist, ispa_split):
+        for l in range(L):
+            if ispa_split and is_l[l]:
+                ispa.ispa_attn_decomp(q[l], ks[l], vs[l], kc[l], vc[l], None, None, w.sm_scale,
+                                      o_local=x)
+            else:
+                ispa.ispa_attn_decomp(q[l], ks[l], vs[l], kc[l], vc[l], kh[l][:n_hist],
+                                      vh[l][:n_hist], w.sm_scale, o_full=x)
+            ispa.ispa_project(x, wo[l], y)
+
+    res = {"frames": list(frames), "l_layers": sum(is_l), "f_layers": L - sum(is_l),
+           "ispa_ms": [], "all_full_ms": [], "speedup": [], "ispa_kv_gb": [], "all_full_kv_gb": []}
+    for fr in frames:
+        n_hist = tok_per_frame * fr
+        times = {}
+        for split in (True, False):
+            chunk(n_hist, split)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                chunk(n_hist, split)
+            e1.record()
+            torch.cuda.synchronize()
+            times[split] = e0.elapsed_time(e1) / reps
+        local = w.n_sink + w.n_cur
+        res["ispa_ms"].append(round(times[True], 2))
+        res["all_full_ms"].append(round(times[False], 2))
+        res["speedup"].append(round(times[False] / times[True], 3))
+        res["ispa_kv_gb"].append(round(kv_tok_bytes * (sum(is_l) * local + (L - sum(is_l)) *
+                                                       (local + n_hist)) / 1e9, 2))
+        res["all_full_kv_gb"].append(round(kv_tok_bytes * L * (local + n_hist) / 1e9, 2))
+        print(f"[bench] stream {fr} frames: ispa {times[True]:.1f} ms, all-full "
+              f"{times[False]:.1f} ms", file=sys.stderr, flush=True)
+    return res
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` (fetch + write, calibrated) from the
+    committed pmc summary, or None when it is missing or was taken on other
+    kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = source_hash(kernel)
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            m = line.strip().strip("|").split("|")
+            if len(m) >= 6 and m[0].strip() == kernel and m[1].strip() == want:
+                return float(m[5])
+    return None
+
+
+def copy_calibration():
+    """A plain 1 GiB device-to-device copy: the reference reading of the HBM
+    byte counters (it reads and writes exactly COPY_BYTES)."""
+    x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, w: wl.Workload):
+    """Markdown table of calibrated HBM bytes per launch for the attention and
+    Gram kernels from the counter_collection CSVs of two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE) of one step of `bench.py --copy-calibration`.
+    Attention figures average the decomposable launches of the warmup pass
+    (the post-absorption chunk that follows them in each step is left out),
+    as the `achieved` throughput does."""
+    n_warm, n_post = w.n_steps * w.n_layers, w.n_layers
+
+    def read(path, counter):
+        with open(path) as f:
+            rows = sorted((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                          for r in csv.DictReader(f) if r["Counter_Name"] == counter)
+        # the calibration copy is the last large copy of the run (smaller
+        # device-to-host reads of the results follow it)
+        copy = [v for _, n, v in rows if "copyBuffer" in n and v > 1024][-1]
+        attn = [v for _, n, v in rows if "attn_decomp_kernel<128>" in n]
+        attn = [v for i, v in enumerate(attn) if i % (n_warm + n_post) < n_warm]
+        gram = [v for _, n, v in rows if "gram_kernel" in n]
+        return copy, {"attn_decomp_kernel<128>": attn, "gram_kernel": gram}
+
+    fc, fe = read(fetch_csv, "FETCH_SIZE")
+    wc, wr = read(write_csv, "WRITE_SIZE")
+    copy_kib = COPY_BYTES / 1024.0
+    f_fac, w_fac = copy_kib / fc, copy_kib / wc
+    run = "python3 $REPO/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-stream --copy-calibration"
+    lines = [
+        f"# HBM traffic per launch: attention and Gram kernels, {w.name}", "",
+        "Commands (run from the repository root on one MI355X):", "", "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o fetch -- {run}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o write -- {run}",
+        "python3 $REPO/bench.py --pmc-summary $REPO/gpurun_out/pmc_fetch/fetch_counter_collection.csv "
+        "$REPO/gpurun_out/pmc_write/write_counter_collection.csv",
+        "```", "",
+        f"Calibration: the plain 1 GiB copy (the last large copy of the run) reads FETCH_SIZE = {fc:.0f} KiB "
+        f"and WRITE_SIZE = {wc:.0f} KiB, so fetch counts are scaled by {f_fac:.4f} and write counts "
+        f"by {w_fac:.4f}.", "",
+        "| kernel | source sha256[:16] | launches | fetch GB/launch | write GB/launch | "
+        "bytes/launch (fetch+write) |",
+        "|---|---|---:|---:|---:|---:|",
+    ]
+    for k in KERNEL_SOURCES:
+        if not fe.get(k) or not wr.get(k):
+            continue
+        fb = sum(fe[k]) / len(fe[k]) * 1024 * f_fac
+        wb = sum(wr[k]) / len(wr[k]) * 1024 * w_fac
+        lines.append(f"| {k} | {source_hash(k)} | {len(fe[k])} | {fb / 1e9:.4f} | {wb / 1e9:.4f} | "
+                     f"{fb + wb:.6g} |")
+    return "\n".join(lines) + "\n"
+
+
+def _short_kernel_name(n: str) -> str:
+    n = n.replace("void ", "").replace("ispa::(anonymous namespace)::", "")
+    if n.startswith("at::native") or "at::native" in n[:40]:
+        return "torch " + n.split("<")[0].split("::")[-1] + " (input generation / restore)"
+    return n.split("(")[0][:70]
+
+
+def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
+    """Markdown summary of a rocprofv3 --kernel-trace CSV of `passes` steps of
+    this script: per-kernel totals, and the attention launches split into the
+    decomposable launches of the warmup pass and the post-absorption chunk."""
+    with open(trace_csv) as f:
+        rows = sorted((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                       int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                      for r in csv.DictReader(f))
+    agg: dict = {}
+    for _, n, dt in rows:
+        k = _short_kernel_name(n)
+        c, t = agg.get(k, (0, 0))
+        agg[k] = (c + 1, t + dt)
+    total = sum(t for _, t in agg.values())
+    n_warm, n_post = w.n_steps * w.n_layers, w.n_layers
+    attn = [dt for _, n, dt in rows if "attn_decomp_kernel<128>" in n]
+    warm = [dt for i, dt in enumerate(attn) if i % (n_warm + n_post) < n_warm]
+    post = [dt for i, dt in enumerate(attn) if i % (n_warm + n_post) >= n_warm]
+    gram = [dt for _, n, dt in rows if "gram_kernel" in n]
+    n_kv = [w.n_sink + w.n_cur + hs for hs in w.hist_per_step]
+    fl = sum(attn_flops(w.n_q, nk, w.hidden) for nk in n_kv) / len(n_kv)
+    lines = [
+        f"# Kernel trace: {w.name}, {passes} steps (1 warmup + 1 timed)", "",
+        "Command (run from the repository root on one MI355X):", "", "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/kt -o kt -- "
+        "python3 $REPO/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-stream",
+        f"python3 $REPO/bench.py --trace-summary $REPO/gpurun_out/kt/kt_kernel_trace.csv",
+        "```", "",
+        "| Kernel | Calls | Avg (us) | Total (ms) | % |", "|---|---:|---:|---:|---:|",
+    ]
+    for k, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        if t / total < 1e-4:
+            continue
+        lines.append(f"| {k} | {c} | {t / c / 1e3:.1f} | {t / 1e6:.2f} | {100 * t / total:.2f} |")
+    if warm:
+        avg = sum(warm) / len(warm)
+        lines += ["", f"Decomposable attention launches of the warmup pass: {len(warm)}, average "
+                  f"{avg / 1e3:.1f} us for {fl / 1e12:.4f} TFLOP each = "
+                  f"{fl / (avg * 1e-9) / 1e12:.1f} TFLOP/s ({100 * fl / (avg * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.1f} % of the "
+                  f"dense bf16 peak)."]
+    if post:
+        lines.append(f"Post-absorption chunk attention launches (L-layers local only, F-layers "
+                     f"full only): {len(post)}, average {sum(post) / len(post) / 1e3:.1f} us.")
+    if gram:
+        avg = sum(gram) / len(gram)
+        gf = gram_flops(w.n_q, w.hidden)
+        lines.append(f"Gram launches: {len(gram)}, average {avg / 1e3:.1f} us for "
+                     f"{gf / 1e9:.1f} GFLOP = {gf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
+    return "\n".join(lines) + "\n"
 
 
 def cpu_baseline(w: wl.Workload, n_rows: int):
@@ -204,7 +454,23 @@ def main():
     ap.add_argument("--workload", default="wan14b_warmup", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the long-horizon streaming comparison (ISPA vs all-full)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB copy (reference for the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--trace-summary", metavar="TRACE_CSV",
+                    help="print the summary of a rocprofv3 --kernel-trace CSV and exit")
     a = ap.parse_args()
+
+    if a.trace_summary:
+        sys.stdout.write(trace_summary(a.trace_summary, wl.WORKLOADS[a.workload], 2))
+        return
+    if a.pmc_summary:
+        sys.stdout.write(pmc_summary(a.pmc_summary[0], a.pmc_summary[1],
+                                     wl.WORKLOADS[a.workload]))
+        return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -234,6 +500,9 @@ def main():
     wall = time.perf_counter() - t0
     print(f"[bench] {a.steps} timed steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
+    if a.copy_calibration:
+        copy_calibration()
+
     tot, n_attn = summarize_events(timing)
     K = a.steps
     n_kv = [w.n_sink + w.n_cur + hs for hs in w.hist_per_step]
@@ -253,8 +522,10 @@ def main():
     gap = (eps[order[w.k_select]] - eps[order[w.k_select - 1]]
            if w.k_select < w.n_layers else None)
 
+    attn_traffic = recorded_traffic("attn_decomp_kernel<128>")
+    kv_bytes = sum(nk * w.n_heads * w.head_dim * 2 * 2 for nk in n_kv) * w.n_layers
     out = {
-        "metric": "decomp-attention TFLOP/s (% bf16 MFMA peak) + dW absorb ms/layer, 14B-class",
+        "metric": METRIC,
         "value": round(attn_tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -281,15 +552,25 @@ def main():
         "gram_ms_per_step": round(tot["gram"] / K, 3),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": attn_traffic,
                      "kernel": "attn_decomp_kernel<128>",
                      "launches_per_step": n_launch,
                      "flop_per_launch_avg": attn_fl / n_launch},
+        "attn_kv_stream_gbs": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
+        "attn_traffic_gbs": (round(attn_traffic / (attn_ms / n_launch * 1e-3) / 1e9, 1)
+                             if attn_traffic else None),
+        "gram_traffic_bytes_per_launch": recorded_traffic("gram_kernel"),
+        "post_absorb_chunk_ms": round(tot["post"] / K, 3),
         "selected_layers": [i for i, s in enumerate(sel) if s],
         "eps_rel_range": [min(eps), max(eps)],
         "eps_gap_at_k": gap,
         "solve_info_nonzero": sum(1 for v in info if v != 0),
     }
+    if not a.no_stream:
+        del inp, ws, timing
+        torch.cuda.empty_cache()
+        out["stream"] = stream_measure(ispa, w)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_rows)
