@@ -9,9 +9,10 @@
 // §3.4 (decomposable attention on online softmax / LSE states, so both come
 // from one attention pass).
 //
-// Work decomposition: one workgroup = one head x 128 queries, 4 waves of 32
-// queries. K/V stream through LDS in 64-key tiles (double buffered, one
-// barrier per tile). Per tile and wave:
+// Work decomposition: one workgroup = one head x 256 queries, 8 waves of 32
+// queries (two per SIMD, one workgroup per CU), so each K/V tile staged in
+// LDS serves 256 queries. K/V stream through LDS in 64-key tiles (double
+// buffered, one barrier per tile). Per tile and wave:
 //   S^T[64 keys x 32 queries] = K Q^T     (16 MFMA 32x32x16, K from LDS,
 //                                          Q^T held in registers)
 //   online softmax on S^T                 (each lane owns one query, so the
@@ -33,8 +34,8 @@
 namespace ispa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kQTile = 128;
+constexpr int kThreads = 512;  // 8 waves
+constexpr int kQTile = 256;
 constexpr int kKTile = 64;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
@@ -59,7 +60,7 @@ template <int D>
 struct TileLoader {
   static constexpr int CPR = D / 8;            // 16-byte chunks per key row
   static constexpr int RPI = 64 / CPR;         // rows per wave instruction
-  static constexpr int IPW = kKTile / RPI / 4; // instructions per wave per tensor
+  static constexpr int IPW = kKTile / RPI / (kThreads / 64); // instructions per wave per tensor
   uint32_t off[IPW];                           // bytes, full tile
   int row[IPW];
   int chunk_off;                               // head * D (elements)
@@ -143,7 +144,7 @@ __device__ __forceinline__ void store_packed(uint16_t* out, const uint32_t (*o)[
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_decomp_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnParams p) {
   constexpr int TBUF = kKTile * D;   // one K or V tile (elements)
   constexpr int NB = D / 32;
   // Four separate LDS arrays (K and V, two buffers each): every access below

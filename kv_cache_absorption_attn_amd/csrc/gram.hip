@@ -23,6 +23,7 @@ constexpr int kThreads = 256;
 constexpr int kT = 128;          // output tile edge
 constexpr int kTok = 64;         // tokens per LDS stage
 constexpr int kBuf = kTok * kT;  // elements of one operand stage (16 KB)
+constexpr int kGroup = 8;        // tile-order group edge (L2 panel sharing)
 
 // Direct-to-LDS loads of one stage of a 128-feature block of Y (token-major
 // rows of 256 bytes, swizzled as lds_swz<128>). Each wave instruction writes
@@ -75,15 +76,41 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
   const int wm = wave / 2, wn = wave % 2;
   const int b = blockIdx.y;
 
-  // tile id -> (bi, bj), bi <= bj, over the 2*nbp block rows of Y^T Y
+  // tile id -> (bi, bj), bi <= bj, over the 2*nbp block rows of Y^T Y. Tiles
+  // are ordered in groups of kGroup x kGroup (upper-triangle groups, row-major)
+  // and each XCD takes a contiguous range of ids, so the ~64 tiles resident on
+  // one XCD cover about kGroup row panels and kGroup column panels of Y: the
+  // panels are fetched once into that XCD's L2 and shared, instead of every
+  // tile streaming its own column panel.
   int idx = xcd_remap(blockIdx.x, n_tiles);
   const int nb2 = 2 * nbp;
-  int bi = 0;
-  while (idx >= nb2 - bi) {
-    idx -= nb2 - bi;
-    ++bi;
+  const int ng = (nb2 + kGroup - 1) / kGroup;
+  int bi = 0, bj = 0;
+  for (int gi = 0; gi < ng; ++gi) {
+    const int ri = min(kGroup, nb2 - gi * kGroup);
+    int gj = gi;
+    for (; gj < ng; ++gj) {
+      const int rj = min(kGroup, nb2 - gj * kGroup);
+      const int size = gj == gi ? ri * (ri + 1) / 2 : ri * rj;
+      if (idx < size) break;
+      idx -= size;
+    }
+    if (gj == ng) continue;
+    if (gj == gi) {  // upper triangle of a diagonal group, row by row
+      int i = 0;
+      while (idx >= ri - i) {
+        idx -= ri - i;
+        ++i;
+      }
+      bi = gi * kGroup + i;
+      bj = bi + idx;
+    } else {
+      const int rj = min(kGroup, nb2 - gj * kGroup);
+      bi = gi * kGroup + idx / rj;
+      bj = gj * kGroup + idx % rj;
+    }
+    break;
   }
-  const int bj = bi + idx;
 
   const int h = p.h;
   const int64_t hh = static_cast<int64_t>(h) * h;
