@@ -9,17 +9,21 @@
 // §3.4 (decomposable attention on online softmax / LSE states, so both come
 // from one attention pass).
 //
-// Work decomposition: one workgroup = one head x 256 queries, 8 waves of 32
-// queries (two per SIMD, one workgroup per CU), so each K/V tile staged in
-// LDS serves 256 queries. K/V stream through LDS in 64-key tiles (double
-// buffered, one barrier per tile). Per tile and wave:
-//   S^T[64 keys x 32 queries] = K Q^T     (16 MFMA 32x32x16, K from LDS,
-//                                          Q^T held in registers)
-//   online softmax on S^T                 (each lane owns one query, so the
-//                                          reductions are in-lane plus one
-//                                          exchange with lane^32)
-//   O^T[d x 32 queries] += V^T P^T        (16 MFMA, V^T from LDS, P^T taken
-//                                          directly from the S^T registers)
+// Work decomposition: one workgroup = one head x 256 queries, 8 waves in 4
+// pairs of 64 queries (two 32-query blocks). In a pair the S-wave computes
+// the scores and the online softmax, the O-wave accumulates the output one
+// tile behind it; both run on one SIMD, so the hardware interleaves the
+// S-wave's exponentials with the O-wave's matrix work. K/V stream through LDS
+// in 64-key tiles (double buffered, one barrier per tile). Per tile and pair:
+//   S-wave: S^T[64 keys x 64 queries] = K Q^T   (32 MFMA 32x32x16, K from LDS
+//           with 16-byte reads, Q^T in registers), then the online softmax on
+//           S^T (each lane owns one query per block: in-lane reductions plus
+//           one exchange between the lane halves), then P^T to LDS in the
+//           MFMA operand layout, with the rescale factors of any move of the
+//           running max.
+//   O-wave: O^T[d x 64 queries] = alpha O^T + V^T P^T   (32 MFMA, V^T by
+//           transposing LDS reads, P^T by 16-byte reads)
+// Each K and V fragment read from LDS feeds two MFMAs (both query blocks).
 // The key order inside V^T is permuted so that the keys a lane holds in its
 // S^T registers are exactly the k-slots of the P^T operand.
 // The running max is only moved when the tile max exceeds it by more than
@@ -34,8 +38,10 @@
 namespace ispa {
 namespace {
 
-constexpr int kThreads = 512;  // 8 waves
-constexpr int kQTile = 256;
+constexpr int kThreads = 512;              // 8 waves: 4 S-waves + 4 O-waves
+constexpr int kPairs = 4;                  // (S-wave, O-wave) pairs
+constexpr int kPairQ = 64;                 // queries per pair: two 32-query blocks
+constexpr int kQTile = kPairs * kPairQ;    // queries per workgroup
 constexpr int kKTile = 64;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
@@ -56,51 +62,50 @@ struct Seg {
 // inside a full tile is fixed, so a full tile only moves a uniform base.
 // In a tail tile, rows past `valid` re-load the last valid row (in bounds);
 // their scores are masked to -inf, so they contribute nothing.
-template <int D>
+template <int D, int NW>
 struct TileLoader {
   static constexpr int CPR = D / 8;            // 16-byte chunks per key row
   static constexpr int RPI = 64 / CPR;         // rows per wave instruction
-  static constexpr int IPW = kKTile / RPI / (kThreads / 64); // instructions per wave per tensor
+  static constexpr int IPW = kKTile / RPI / NW; // instructions per wave per tensor
   uint32_t off[IPW];                           // bytes, full tile
-  int row[IPW];
-  int chunk_off;                               // head * D (elements)
+  int row[IPW];                                // tile row of the lane's chunk
+  int col[IPW];                                // head * D + 8 * chunk (elements)
   int lds_base;                                // elements
 
-  __device__ void init(int64_t rs, int head, int wave, int lane) {
-    const int p = lane % CPR;
-    chunk_off = head * D;
-    lds_base = wave * IPW * RPI * D;
+  // `w` in [0, NW): this wave's share of the tile rows
+  __device__ void init(int64_t rs, int head, int w, int lane) {
+    lds_base = w * IPW * RPI * D;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      row[i] = (wave * IPW + i) * RPI + lane / CPR;
-      const int c = p ^ swz<D>(row[i]);
-      off[i] = static_cast<uint32_t>((row[i] * rs + head * D + 8 * c) * 2);
+      row[i] = (w * IPW + i) * RPI + lane / CPR;
+      col[i] = head * D + 8 * ((lane % CPR) ^ swz<D>(row[i]));
+      off[i] = static_cast<uint32_t>((row[i] * rs + col[i]) * 2);
     }
   }
 
-  __device__ void issue(const Seg& sg, int64_t row0, int valid, int64_t rs, uint16_t* ks,
-                        uint16_t* vs, int lane) const {
-    const char* kb = reinterpret_cast<const char*>(sg.k + row0 * rs);
-    const char* vb = reinterpret_cast<const char*>(sg.v + row0 * rs);
+  // Loads this wave's rows of one tile of K (issue_k) or V (issue_v).
+  __device__ void issue_k(const Seg& sg, int64_t row0, int valid, int64_t rs,
+                          uint16_t* dst) const {
+    issue(sg.k, row0, valid, rs, dst);
+  }
+  __device__ void issue_v(const Seg& sg, int64_t row0, int valid, int64_t rs,
+                          uint16_t* dst) const {
+    issue(sg.v, row0, valid, rs, dst);
+  }
+  __device__ void issue(const uint16_t* src, int64_t row0, int valid, int64_t rs,
+                        uint16_t* dst) const {
+    const char* b = reinterpret_cast<const char*>(src + row0 * rs);
     if (valid == kKTile) {
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        __builtin_amdgcn_global_load_lds(kb + off[i], ISPA_LDS(void, ks + lds_base + i * RPI * D),
+      for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_global_load_lds(b + off[i], ISPA_LDS(void, dst + lds_base + i * RPI * D),
                                          16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + off[i], ISPA_LDS(void, vs + lds_base + i * RPI * D),
-                                         16, 0, 0);
-      }
     } else {
-      const int p = lane % CPR;
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int rr = row[i] < valid ? row[i] : valid - 1;
-        const int c = p ^ swz<D>(row[i]);
-        const int64_t o = (rr * rs + chunk_off + 8 * c) * 2;
-        __builtin_amdgcn_global_load_lds(kb + o, ISPA_LDS(void, ks + lds_base + i * RPI * D), 16,
-                                         0, 0);
-        __builtin_amdgcn_global_load_lds(vb + o, ISPA_LDS(void, vs + lds_base + i * RPI * D), 16,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds(b + (rr * rs + col[i]) * 2,
+                                         ISPA_LDS(void, dst + lds_base + i * RPI * D), 16, 0, 0);
       }
     }
   }
@@ -129,16 +134,20 @@ __device__ __forceinline__ void store_o(uint16_t* out, const f32x16* o, int64_t 
   }
 }
 
+// Inverse of store_o: the bf16 values of a row block, as fp32.
 template <int D>
-__device__ __forceinline__ void store_packed(uint16_t* out, const uint32_t (*o)[8], int64_t qi,
-                                             int64_t rs, int head, int hf) {
-  uint16_t* row = out + qi * rs + head * D;
+__device__ __forceinline__ void load_o(const uint16_t* in, f32x16* o, int64_t qi, int64_t rs,
+                                       int head, int hf) {
+  const uint16_t* row = in + qi * rs + head * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int d = 32 * db + 8 * g + 4 * hf;
-      *reinterpret_cast<uint2*>(row + d) = make_uint2(o[db][2 * g], o[db][2 * g + 1]);
+      const uint2 val = *reinterpret_cast<const uint2*>(row + 32 * db + 8 * g + 4 * hf);
+      o[db][4 * g + 0] = __uint_as_float(val.x << 16);
+      o[db][4 * g + 1] = __uint_as_float(val.x & 0xFFFF0000u);
+      o[db][4 * g + 2] = __uint_as_float(val.y << 16);
+      o[db][4 * g + 3] = __uint_as_float(val.y & 0xFFFF0000u);
     }
   }
 }
@@ -146,33 +155,40 @@ __device__ __forceinline__ void store_packed(uint16_t* out, const uint32_t (*o)[
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnParams p) {
   constexpr int TBUF = kKTile * D;   // one K or V tile (elements)
-  constexpr int NB = D / 32;
-  // Four separate LDS arrays (K and V, two buffers each): every access below
-  // names a fixed array, so the compiler can see that the prefetch into one
-  // buffer never aliases the reads of the other and needs no early wait.
+  constexpr int NB = D / 32;         // 32-wide d blocks of O^T
+  constexpr int NT = D / 16;         // k-steps of K Q^T
+  constexpr int PSLOT = kPairs * 2 * 4 * 64;  // P^T operands of one tile (16-byte units)
+  // K and V tiles, two buffers each, and the P^T hand-off, two slots: every
+  // access names a fixed array, so the compiler can see that a load into one
+  // buffer never aliases the reads of another and needs no early wait.
   __shared__ __attribute__((aligned(16))) uint16_t sk0[TBUF];
   __shared__ __attribute__((aligned(16))) uint16_t sk1[TBUF];
   __shared__ __attribute__((aligned(16))) uint16_t sv0[TBUF];
   __shared__ __attribute__((aligned(16))) uint16_t sv1[TBUF];
+  __shared__ uint4 sp0[PSLOT];                 // [pair][qb][st][lane]
+  __shared__ uint4 sp1[PSLOT];
+  __shared__ float sal0[kPairs * 64];          // rescale factor per query [pair][qb*32+q]
+  __shared__ float sal1[kPairs * 64];
+  __shared__ int sfl0[kPairs];                 // any query of the pair rescaled
+  __shared__ int sfl1[kPairs];
+  __shared__ float s_inv_loc[kPairs * 64];     // 1 / l of the local phase
+  __shared__ float s_inv_fin[kPairs * 64];     // 1 / l of the history (or only) phase
+  __shared__ float s_wh[kPairs * 64];          // merge weight w_H
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, l32 = lane % 32, hf = lane / 32;
+  const int pair = wave % kPairs;
+  const bool s_role = wave < kPairs;
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int head = work / p.n_qtiles;
   const int qt = work % p.n_qtiles;
   const int64_t rs = static_cast<int64_t>(p.n_heads) * D;
-  const int64_t qi = static_cast<int64_t>(qt) * kQTile + wave * 32 + l32;
-  const bool qvalid = qi < p.n_q;
-
-  // Q^T operand fragments, held for the whole pass.
-  bf16x8 qf[D / 16];
+  int64_t qi[2];
+  bool qvalid[2];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    if (qvalid) {
-      qf[t] = *reinterpret_cast<const bf16x8*>(p.q + qi * rs + head * D + 16 * t + 8 * hf);
-    } else {
-      qf[t] = bf16x8{};
-    }
+  for (int qb = 0; qb < 2; ++qb) {
+    qi[qb] = static_cast<int64_t>(qt) * kQTile + pair * kPairQ + 32 * qb + l32;
+    qvalid[qb] = qi[qb] < p.n_q;
   }
 
   const int nt0 = static_cast<int>((p.n[0] + kKTile - 1) / kKTile);
@@ -183,8 +199,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
   const bool run_hist = !(split && !p.need_hist);
   const int T = n_local_tiles + (run_hist ? nt2 : 0);
 
-  // Flat tile index -> (segment pointers, first row, valid rows). Selected
-  // with conditionals so nothing is indexed dynamically (no scratch).
   auto tile_of = [&](int idx, Seg& sg, int64_t& row0, int& valid) {
     const bool s0 = idx < nt0, s1 = !s0 && idx < n_local_tiles;
     const int t = s0 ? idx : (s1 ? idx - nt0 : idx - n_local_tiles);
@@ -196,193 +210,316 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
     valid = rem < kKTile ? static_cast<int>(rem) : kKTile;
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 oacc[NB];
+  TileLoader<D, kPairs> loader;
+  loader.init(rs, head, pair, lane);
+  const int prow = pair * 64;  // this pair's entries in the per-query arrays
+
+  if (s_role) {
+    // ------------------------------------------------------------ S-wave
+    // Scores, online softmax statistics and P of every tile; P^T goes to the
+    // pair's O-wave through LDS together with the rescale factors.
+    bf16x8 qf[2][NT];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) oacc[b] = f32x16{};
-  // O_local kept as its bf16 output values (the X the statistics see) while
-  // the history phase runs: D is then formed against exactly that X.
-  uint32_t o_loc[NB][8];
-  float lse_loc2 = -INFINITY;
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        qf[qb][t] = qvalid[qb] ? *reinterpret_cast<const bf16x8*>(p.q + qi[qb] * rs + head * D +
+                                                                  16 * t + 8 * hf)
+                               : bf16x8{};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    float lse_loc2[2] = {-INFINITY, -INFINITY};
+    {
+      Seg sg;
+      int valid;
+      int64_t row0;
+      tile_of(0, sg, row0, valid);
+      loader.issue_k(sg, row0, valid, rs, sk0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 
+    auto s_step = [&](auto buf_c, int it) {
+      constexpr int BUF = decltype(buf_c)::value;
+      const uint16_t* __restrict__ ks = BUF ? sk1 : sk0;
+      uint16_t* __restrict__ nks = BUF ? sk0 : sk1;
+      uint4* __restrict__ sp = BUF ? sp1 : sp0;
+      float* __restrict__ sal = BUF ? sal1 : sal0;
+      int* __restrict__ sfl = BUF ? sfl1 : sfl0;
+      if (it < T) {
+        Seg sg;
+        int valid;
+        int64_t row0;
+        if (it + 1 < T) {
+          tile_of(it + 1, sg, row0, valid);
+          loader.issue_k(sg, row0, valid, rs, nks);
+        }
+        tile_of(it, sg, row0, valid);
 
-  TileLoader<D> loader;
-  loader.init(rs, head, wave, lane);
-  {
-    Seg sg;
-    int valid;
-    int64_t row0;
-    tile_of(0, sg, row0, valid);
-    loader.issue(sg, row0, valid, rs, sk0, sv0, lane);
+        // S^T[key half][query block] = K Q^T
+        f32x16 sc[2][2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) sc[kh][qb] = f32x16{};
+        // K fragments are read one k-step ahead of their MFMAs (the
+        // scheduling barriers keep the loads from being hoisted further,
+        // which would only cost registers: the O-wave on the same SIMD hides
+        // the latency)
+        bf16x8 a0 = k_frag<D>(ks, l32, hf), a1 = k_frag<D>(ks, 32 + l32, hf);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          bf16x8 n0, n1;
+          if (t + 1 < NT) {
+            n0 = k_frag<D>(ks, l32, 2 * (t + 1) + hf);
+            n1 = k_frag<D>(ks, 32 + l32, 2 * (t + 1) + hf);
+          }
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            sc[0][qb] = mfma32x32x16(a0, qf[qb][t], sc[0][qb]);
+            sc[1][qb] = mfma32x32x16(a1, qf[qb][t], sc[1][qb]);
+          }
+          a0 = n0;
+          a1 = n1;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // A tail tile's rows past `valid` re-load the last valid key: their
+        // scores duplicate real ones (the row maxima need no mask) and only
+        // their exponentials are dropped, in a separate instance of the
+        // softmax code so the common path carries no masking.
+        auto softmax = [&](auto tail_c) {
+          constexpr bool TAIL = decltype(tail_c)::value;
+          // running max: moved only when the tile max exceeds it by more than
+          // the threshold; the O-wave applies the same factor to its sums
+          bool need[2];
+          float alpha[2], mt[2];
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            float mx = sc[0][qb][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][qb][i]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][qb][i]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                             __float_as_uint(mx), false, false);
+            mt[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+            need[qb] = mt[qb] > m_run[qb] + kRescaleThreshold;
+            alpha[qb] = 1.f;
+          }
+          const bool any = __any(need[0] || need[1]);
+          if (any) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              if (need[qb]) {
+                alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - mt[qb]);
+                m_run[qb] = mt[qb];
+                l_run[qb] *= alpha[qb];
+              }
+              if (hf == 0) sal[prow + 32 * qb + l32] = alpha[qb];
+            }
+          }
+          if (lane == 0) sfl[pair] = any ? 1 : 0;
+
+          // P = 2^(s * scale_log2 - m): row sums in fp32 (the LSE needs them),
+          // P^T to LDS rounded to bf16, lane-major in the MFMA operand layout.
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            float lsum = 0.f;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              bf16x8 pv;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                float e = __builtin_amdgcn_exp2f(
+                    fmaf(sc[st / 2][qb][8 * (st % 2) + i], p.scale_log2, -m_run[qb]));
+                if constexpr (TAIL) {
+                  const int key = 32 * (st / 2) + 8 * ((8 * (st % 2) + i) / 4) + 4 * hf + (i % 4);
+                  if (key >= valid) e = 0.f;
+                }
+                lsum += e;
+                pv[i] = static_cast<__bf16>(e);
+              }
+              sp[((pair * 2 + qb) * 4 + st) * 64 + lane] = __builtin_bit_cast(uint4, pv);
+            }
+            l_run[qb] += lsum;
+          }
+        };
+        if (valid == kKTile) {
+          softmax(std::false_type{});
+        } else {
+          asm volatile("" ::: "memory");
+          softmax(std::true_type{});
+        }
+
+        if (split && it == n_local_tiles - 1) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+            lse_loc2[qb] = m_run[qb] + __builtin_amdgcn_logf(lt);
+            if (hf == 0) s_inv_loc[prow + 32 * qb + l32] = 1.f / lt;
+            if (qvalid[qb] && p.lse_local && hf == 0)
+              p.lse_local[head * p.n_q + qi[qb]] = lse_loc2[qb] * kLn2;
+            m_run[qb] = -INFINITY;
+            l_run[qb] = 0.f;
+          }
+        }
+      } else {
+        // after the last tile: final statistics for the O-wave's epilogue
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+          float inv = 0.f, lse2 = -INFINITY, w_h = 0.f, lse_f2;
+          if (!split) {
+            inv = 1.f / lt;
+            lse_f2 = m_run[qb] + __builtin_amdgcn_logf(lt);
+          } else {
+            if (p.n[2] > 0) {
+              inv = 1.f / lt;
+              lse2 = m_run[qb] + __builtin_amdgcn_logf(lt);
+            }
+            lse_f2 = lse_loc2[qb];
+            if (p.n[2] > 0) {
+              const float mm = fmaxf(lse_loc2[qb], lse2);
+              lse_f2 = mm + __builtin_amdgcn_logf(__builtin_amdgcn_exp2f(lse_loc2[qb] - mm) +
+                                                  __builtin_amdgcn_exp2f(lse2 - mm));
+              w_h = __builtin_amdgcn_exp2f(lse2 - lse_f2);
+            }
+          }
+          if (hf == 0) {
+            s_inv_fin[prow + 32 * qb + l32] = inv;
+            s_wh[prow + 32 * qb + l32] = w_h;
+            if (qvalid[qb]) {
+              if (split && p.need_hist && p.lse_hist)
+                p.lse_hist[head * p.n_q + qi[qb]] = lse2 * kLn2;
+              if ((!split || p.need_hist) && p.lse_full)
+                p.lse_full[head * p.n_q + qi[qb]] = lse_f2 * kLn2;
+            }
+          }
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+    for (int it = 0; it <= T; it += 2) {
+      s_step(std::integral_constant<int, 0>{}, it);
+      if (it + 1 <= T) s_step(std::integral_constant<int, 1>{}, it + 1);
+    }
+    return;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
 
-  // One tile; BUF (compile time) selects the LDS buffers it reads, the
-  // prefetch of the next tile goes to the other pair.
-  auto tile_step = [&](auto buf_c, int idx) {
+  // -------------------------------------------------------------- O-wave
+  // O^T += V^T P^T one tile behind the S-wave, with its rescale factors.
+  f32x16 oacc[2][NB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) oacc[qb][b] = f32x16{};
+  // O_local is kept as its bf16 output values (the X the statistics see)
+  // while the history phase runs, so D is formed against exactly that X: it
+  // is parked in an output row this lane owns (O_local if requested, else
+  // O_full, else D; each is written with its final value only after the
+  // parked X has been read back). With none of them requested, no merge is
+  // formed and X is not needed.
+  uint16_t* const park = p.o_local ? p.o_local : (p.o_full ? p.o_full : p.d_out);
+  __syncthreads();  // K of tile 0 staged (the S-waves' prologue)
+
+  auto o_step = [&](auto buf_c, int it) {
     constexpr int BUF = decltype(buf_c)::value;
-    const uint16_t* ks = BUF ? sk1 : sk0;
-    const uint16_t* vs = BUF ? sv1 : sv0;
-    uint16_t* nks = BUF ? sk0 : sk1;
-    uint16_t* nvs = BUF ? sv0 : sv1;
-    Seg sg;
-    int valid;
-    int64_t row0;
-    tile_of(idx, sg, row0, valid);
-    const bool has_next = idx + 1 < T;
-    if (has_next) {
-      Seg s2;
-      int v2;
-      int64_t r2;
-      tile_of(idx + 1, s2, r2, v2);
-      loader.issue(s2, r2, v2, rs, nks, nvs, lane);
+    const uint16_t* __restrict__ vs = BUF ? sv0 : sv1;   // V of tile it-1
+    uint16_t* __restrict__ nvs = BUF ? sv1 : sv0;        // V of tile it
+    const uint4* __restrict__ sp = BUF ? sp0 : sp1;      // P of tile it-1
+    const float* __restrict__ sal = BUF ? sal0 : sal1;
+    const int* __restrict__ sfl = BUF ? sfl0 : sfl1;
+    if (it < T) {
+      Seg sg;
+      int valid;
+      int64_t row0;
+      tile_of(it, sg, row0, valid);
+      loader.issue_v(sg, row0, valid, rs, nvs);
     }
-
-    // S^T = K Q^T
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    if (it >= 1) {
+      const int jb = it - 1;
+      if (__builtin_amdgcn_readfirstlane(sfl[pair])) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const bf16x8 a0 = k_frag<D>(ks, l32, 2 * t + hf);
-      const bf16x8 a1 = k_frag<D>(ks, 32 + l32, 2 * t + hf);
-      s0 = mfma32x32x16(a0, qf[t], s0);
-      s1 = mfma32x32x16(a1, qf[t], s1);
-    }
-
-    if (valid < kKTile) {
-      // tail tile only: keep this a real branch (the empty volatile asm stops
-      // it from being flattened into unconditional selects)
-      asm volatile("" ::: "memory");
+        for (int qb = 0; qb < 2; ++qb) {
+          const float a = sal[prow + 32 * qb + l32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 8 * (i / 4) + 4 * hf + (i % 4);
-        if (key >= valid) s0[i] = -INFINITY;
-        if (key + 32 >= valid) s1[i] = -INFINITY;
+          for (int b = 0; b < NB; ++b) oacc[qb][b] *= a;
+        }
+      }
+      // V^T operands one step ahead of their MFMAs, P^T operands one key
+      // step ahead (bounded by scheduling barriers, as in the S-wave)
+      auto pfrag = [&](int qb, int st) {
+        return __builtin_bit_cast(bf16x8, sp[((pair * 2 + qb) * 4 + st) * 64 + lane]);
+      };
+      bf16x8 p0 = pfrag(0, 0), p1 = pfrag(1, 0);
+      bf16x8 va = tr_operand<D>(vs, 0, 0, lane);
+#pragma unroll
+      for (int u = 0; u < 4 * NB; ++u) {
+        const int st = u / NB, db = u % NB;
+        bf16x8 vn, q0, q1;
+        if (u + 1 < 4 * NB) vn = tr_operand<D>(vs, 16 * ((u + 1) / NB), 32 * ((u + 1) % NB), lane);
+        if (db == 0 && st + 1 < 4) {
+          q0 = pfrag(0, st + 1);
+          q1 = pfrag(1, st + 1);
+        }
+        oacc[0][db] = mfma32x32x16(va, p0, oacc[0][db]);
+        oacc[1][db] = mfma32x32x16(va, p1, oacc[1][db]);
+        va = vn;
+        if (db == NB - 1) {
+          p0 = q0;
+          p1 = q1;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (split && jb == n_local_tiles - 1) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float inv = s_inv_loc[prow + 32 * qb + l32];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) oacc[qb][b] *= inv;
+          if (qvalid[qb] && park) store_o<D>(park, oacc[qb], qi[qb], rs, head, hf);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) oacc[qb][b] = f32x16{};
+        }
       }
     }
-
-    float mx = s0[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = mx * p.scale_log2;
-    const bool need = mt > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float mnew = need ? mt : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-      m_run = mnew;
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) oacc[b] *= alpha;
-    }
-
-    // P = 2^(s * scale_log2 - m); the row sum is kept in fp32 (the LSE needs
-    // it), P goes to the PV product rounded to bf16.
-    bf16x8 pf[4];
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[i], p.scale_log2, -m_run));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[i], p.scale_log2, -m_run));
-      lsum += e0 + e1;
-      pf[i / 8][i % 8] = static_cast<__bf16>(e0);
-      pf[2 + i / 8][i % 8] = static_cast<__bf16>(e1);
-    }
-    l_run += lsum;
-
-    // O^T += V^T P^T, key step outer so consecutive MFMAs feed independent
-    // accumulators
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-      for (int db = 0; db < NB; ++db) {
-        const bf16x8 a = tr_operand<D>(vs, 16 * st, 32 * db, lane);
-        oacc[db] = mfma32x32x16(a, pf[st], oacc[db]);
-      }
-    }
-
-
-    if (split && idx == n_local_tiles - 1) {
-      const float lt = l_run + __shfl_xor(l_run, 32);
-      const float inv = 1.f / lt;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w)
-          o_loc[b][w] = pack_bf16x2(oacc[b][2 * w] * inv, oacc[b][2 * w + 1] * inv);
-      }
-      lse_loc2 = m_run + __builtin_amdgcn_logf(lt);
-      if (qvalid) {
-        if (p.o_local) store_packed<D>(p.o_local, o_loc, qi, rs, head, hf);
-        if (p.lse_local && hf == 0) p.lse_local[head * p.n_q + qi] = lse_loc2 * kLn2;
-      }
-      m_run = -INFINITY;
-      l_run = 0.f;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) oacc[b] = f32x16{};
-    }
-    // the next tile's direct-to-LDS loads (issued at the top) must land
-    // before any wave reads them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  for (int idx = 0; idx < T; idx += 2) {
-    tile_step(std::integral_constant<int, 0>{}, idx);
-    if (idx + 1 < T) tile_step(std::integral_constant<int, 1>{}, idx + 1);
+  for (int it = 0; it <= T; it += 2) {
+    o_step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 <= T) o_step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  if (!qvalid) return;
-  if (!split) {
-    const float lt = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / lt;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) oacc[b] *= inv;
-    if (p.o_full) store_o<D>(p.o_full, oacc, qi, rs, head, hf);
-    if (p.lse_full && hf == 0)
-      p.lse_full[head * p.n_q + qi] = (m_run + __builtin_amdgcn_logf(lt)) * kLn2;
-    return;
-  }
-  if (!p.need_hist) return;
-
-  // History result (O_H = 0, LSE_H = -inf for an empty history).
-  float lse_h2 = -INFINITY;
-  if (p.n[2] > 0) {
-    const float lt = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / lt;
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!qvalid[qb]) continue;
+    const float inv = s_inv_fin[prow + 32 * qb + l32];
+    if (!split) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) oacc[b] *= inv;
-    lse_h2 = m_run + __builtin_amdgcn_logf(lt);
-  }
-  if (p.o_hist) store_o<D>(p.o_hist, oacc, qi, rs, head, hf);
-  if (p.lse_hist && hf == 0) p.lse_hist[head * p.n_q + qi] = lse_h2 * kLn2;
-
-  // LSE merge: w_H = 2^(LSE_H - LSE_F), D = w_H (O_H - O_L), O_F = O_L + D.
-  float lse_f2 = lse_loc2, w_h = 0.f;
-  if (p.n[2] > 0) {
-    const float mm = fmaxf(lse_loc2, lse_h2);
-    lse_f2 = mm + __builtin_amdgcn_logf(__builtin_amdgcn_exp2f(lse_loc2 - mm) +
-                                        __builtin_amdgcn_exp2f(lse_h2 - mm));
-    w_h = __builtin_amdgcn_exp2f(lse_h2 - lse_f2);
-  }
-  f32x16 xl[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      xl[b][2 * w] = __uint_as_float(o_loc[b][w] << 16);
-      xl[b][2 * w + 1] = __uint_as_float(o_loc[b][w] & 0xFFFF0000u);
+      for (int b = 0; b < NB; ++b) oacc[qb][b] *= inv;
+      if (p.o_full) store_o<D>(p.o_full, oacc[qb], qi[qb], rs, head, hf);
+      continue;
     }
-    oacc[b] = (oacc[b] - xl[b]) * w_h;  // D
-  }
-  if (p.d_out) store_o<D>(p.d_out, oacc, qi, rs, head, hf);
-  if (p.o_full) {
+    if (!p.need_hist) continue;
+    // history result (O_H = 0 for an empty history), then the LSE merge:
+    // D = w_H (O_H - O_L), O_F = O_L + D
 #pragma unroll
-    for (int b = 0; b < NB; ++b) oacc[b] += xl[b];
-    store_o<D>(p.o_full, oacc, qi, rs, head, hf);
+    for (int b = 0; b < NB; ++b) oacc[qb][b] *= inv;
+    if (p.o_hist) store_o<D>(p.o_hist, oacc[qb], qi[qb], rs, head, hf);
+    if (!park) continue;
+    const float w_h = s_wh[prow + 32 * qb + l32];
+    f32x16 xl[NB];
+    load_o<D>(park, xl, qi[qb], rs, head, hf);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) oacc[qb][b] = (oacc[qb][b] - xl[b]) * w_h;
+    if (p.d_out) store_o<D>(p.d_out, oacc[qb], qi[qb], rs, head, hf);
+    if (p.o_full) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) oacc[qb][b] += xl[b];
+      store_o<D>(p.o_full, oacc[qb], qi[qb], rs, head, hf);
+    }
   }
-  if (p.lse_full && hf == 0) p.lse_full[head * p.n_q + qi] = lse_f2 * kLn2;
 }
 
 
