@@ -93,6 +93,35 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* base, int row0, int
                                  __builtin_bit_cast(bf16x4_local, hi), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Lane offsets (elements) of the two transposing reads of tr_operand for
+// operand columns col0.. of a swizzled tile, for row0 = 0. The swizzle only
+// depends on row % 16, so for any row0 that is a multiple of 16 the reads are
+// at base + row0 * D + off: the offsets are computed once and every k-step
+// only adds a compile-time immediate.
+struct TrOff {
+  int lo, hi;
+};
+template <int D>
+__device__ __forceinline__ TrOff tr_offsets(int col0, int lane) {
+  const int g = lane / 16, i = lane % 16;
+  const int r = 4 * (g / 2) + i / 4;
+  const int c = col0 + 16 * (g % 2) + 4 * (i % 4);
+  TrOff o;
+  o.lo = r * D + 8 * ((c >> 3) ^ lds_swz<D>(r)) + (c & 7);
+  o.hi = (r + 8) * D + 8 * ((c >> 3) ^ lds_swz<D>(r + 8)) + (c & 7);
+  return o;
+}
+
+// tr_operand with precomputed lane offsets; row0 % 16 == 0.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand_at(const uint16_t* base, int row0, TrOff o) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS(s16x4, base + row0 * D + o.lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ISPA_LDS(s16x4, base + row0 * D + o.hi));
+  typedef __bf16 bf16x4_local __attribute__((ext_vector_type(4)));
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4_local, lo),
+                                 __builtin_bit_cast(bf16x4_local, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X. Remap
 // the hardware block id so that consecutive logical work items land on the
 // same XCD (and share its L2): logical id = start(xcd) + bid / 8.

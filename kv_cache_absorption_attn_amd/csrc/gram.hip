@@ -32,8 +32,9 @@ constexpr int kGroup = 8;        // tile-order group edge (L2 panel sharing)
 // here and zeroed in LDS afterwards.
 struct GramLoader {
   int row[4];
-  int col[4];   // element offset of the lane's 16-byte chunk within the block
-  __device__ void init(int wave, int lane, int fvalid) {
+  uint32_t off[4];  // byte offset of the lane's 16-byte chunk from the stage's first row
+  int col[4];       // element offset of that chunk within the block
+  __device__ void init(int wave, int lane, int fvalid, int h) {
     const int p = lane % 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -41,10 +42,20 @@ struct GramLoader {
       int c = p ^ lds_swz<kT>(row[i]);
       if (8 * c >= fvalid) c = fvalid / 8 - 1;
       col[i] = 8 * c;
+      off[i] = static_cast<uint32_t>((row[i] * h + col[i]) * 2);
     }
   }
-  __device__ void issue(const uint16_t* src, int h, int64_t t0, int64_t n_tok,
-                        uint16_t* dst, int wave) const {
+  // A full stage: a uniform base plus the fixed lane offsets.
+  __device__ void issue(const uint16_t* src, int h, int64_t t0, uint16_t* dst, int wave) const {
+    const char* b = reinterpret_cast<const char*>(src + t0 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(b + off[i]),
+                                       ISPA_LDS(void, dst + (wave * 4 + i) * 4 * kT), 16, 0, 0);
+  }
+  // The last (partial) stage: token rows past n_tok re-load the last token.
+  __device__ void issue_tail(const uint16_t* src, int h, int64_t t0, int64_t n_tok, uint16_t* dst,
+                             int wave) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int64_t t = t0 + row[i];
@@ -129,8 +140,14 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
   if (dest == nullptr) return;
 
   GramLoader li, lj;
-  li.init(wave, lane, fvi);
-  lj.init(wave, lane, fvj);
+  li.init(wave, lane, fvi, h);
+  lj.init(wave, lane, fvj, h);
+  TrOff oa[2], ob[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    oa[i] = tr_offsets<kT>(wm * 64 + i * 32, lane);
+    ob[i] = tr_offsets<kT>(wn * 64 + i * 32, lane);
+  }
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -139,9 +156,18 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
 
   const int nst = static_cast<int>((p.n_tok + kTok - 1) / kTok);
   const int tail = static_cast<int>(p.n_tok - static_cast<int64_t>(nst - 1) * kTok);
+  auto issue_stage = [&](int s, uint16_t* da, uint16_t* db_) {
+    const int64_t t0 = static_cast<int64_t>(s) * kTok;
+    if (t0 + kTok <= p.n_tok) {
+      li.issue(srci, h, t0, da, wave);
+      lj.issue(srcj, h, t0, db_, wave);
+    } else {
+      li.issue_tail(srci, h, t0, p.n_tok, da, wave);
+      lj.issue_tail(srcj, h, t0, p.n_tok, db_, wave);
+    }
+  };
   if (nst > 0) {
-    li.issue(srci, h, 0, p.n_tok, sa0, wave);
-    lj.issue(srcj, h, 0, p.n_tok, sb0, wave);
+    issue_stage(0, sa0, sb0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (nst == 1 && tail < kTok) {
@@ -157,17 +183,14 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
   auto stage = [&](int s, const uint16_t* __restrict__ ra, const uint16_t* __restrict__ rb,
                    uint16_t* __restrict__ na, uint16_t* __restrict__ nb) {
     const bool has_next = s + 1 < nst;
-    if (has_next) {
-      li.issue(srci, h, static_cast<int64_t>(s + 1) * kTok, p.n_tok, na, wave);
-      lj.issue(srcj, h, static_cast<int64_t>(s + 1) * kTok, p.n_tok, nb, wave);
-    }
+    if (has_next) issue_stage(s + 1, na, nb);
 #pragma unroll
     for (int st = 0; st < kTok / 16; ++st) {
       bf16x8 a[2], bv[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = tr_operand<kT>(ra, 16 * st, wm * 64 + i * 32, lane);
+      for (int i = 0; i < 2; ++i) a[i] = tr_operand_at<kT>(ra, 16 * st, oa[i]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bv[j] = tr_operand<kT>(rb, 16 * st, wn * 64 + j * 32, lane);
+      for (int j = 0; j < 2; ++j) bv[j] = tr_operand_at<kT>(rb, 16 * st, ob[j]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
