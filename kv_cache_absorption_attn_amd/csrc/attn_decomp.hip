@@ -12,8 +12,9 @@
 // Work decomposition: one workgroup = one head x 256 queries, 8 waves in 4
 // pairs of 64 queries (two 32-query blocks). In a pair the S-wave computes
 // the scores and the online softmax, the O-wave accumulates the output one
-// tile behind it; both run on one SIMD, so the hardware interleaves the
-// S-wave's exponentials with the O-wave's matrix work. K/V stream through LDS
+// tile behind it; both run on one SIMD. A mid-step barrier holds the O-wave's
+// PV until the S-wave has issued its K Q^T, so the PV runs during the
+// softmax (vector ALU) rather than against the K Q^T (matrix cores). K/V stream through LDS
 // in 64-key tiles (double buffered, one barrier per tile). Per tile and pair:
 //   S-wave: S^T[64 keys x 64 queries] = K Q^T   (32 MFMA 32x32x16, K from LDS
 //           with 16-byte reads, Q^T in registers), then the online softmax on
@@ -294,11 +295,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
           float alpha[2], mt[2];
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
-            float mx = sc[0][qb][0];
+            // 4-way tree: short dependency chains
+            float m4[4];
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][qb][i]);
+            for (int k = 0; k < 4; ++k) m4[k] = fmaxf(sc[0][qb][k], sc[1][qb][k]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][qb][i]);
+            for (int i = 4; i < 16; ++i) {
+              m4[i % 4] = fmaxf(m4[i % 4], sc[0][qb][i]);
+              m4[i % 4] = fmaxf(m4[i % 4], sc[1][qb][i]);
+            }
+            const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
                                                              __float_as_uint(mx), false, false);
             mt[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
           // P^T to LDS rounded to bf16, lane-major in the MFMA operand layout.
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
-            float lsum = 0.f;
+            float lsum4[4] = {0.f, 0.f, 0.f, 0.f};  // one partial sum per key step
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
               bf16x8 pv;
@@ -335,14 +341,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
                   const int key = 32 * (st / 2) + 8 * ((8 * (st % 2) + i) / 4) + 4 * hf + (i % 4);
                   if (key >= valid) e = 0.f;
                 }
-                lsum += e;
+                lsum4[st] += e;
                 pv[i] = static_cast<__bf16>(e);
               }
               sp[((pair * 2 + qb) * 4 + st) * 64 + lane] = __builtin_bit_cast(uint4, pv);
             }
-            l_run[qb] += lsum;
+            l_run[qb] += (lsum4[0] + lsum4[1]) + (lsum4[2] + lsum4[3]);
           }
         };
+        // the O-wave starts its PV only now, so its matrix work overlaps the
+        // softmax below instead of competing with the K Q^T above
+        __builtin_amdgcn_s_barrier();
         if (valid == kKTile) {
           softmax(std::false_type{});
         } else {
@@ -363,6 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
           }
         }
       } else {
+        __builtin_amdgcn_s_barrier();
         // after the last tile: final statistics for the O-wave's epilogue
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -436,6 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
       tile_of(it, sg, row0, valid);
       loader.issue_v(sg, row0, valid, rs, nvs);
     }
+    __builtin_amdgcn_s_barrier();  // the S-wave has issued its K Q^T
     if (it >= 1) {
       const int jb = it - 1;
       if (__builtin_amdgcn_readfirstlane(sfl[pair])) {
