@@ -65,6 +65,55 @@ hipError_t gemm(int M, int N, int K, const void* A, int64_t a_s0, int64_t a_s1, 
   return ispa::launch_gemm_f32(p, s);
 }
 
+// Block rows [ba, bb) of R (128 rows per block, the last one possibly short).
+inline int blk_row(int b, int h) { return b * kCholBlock < h ? b * kCholBlock : h; }
+
+// R[rows of blocks ba..bb) <- L^-1 R for the lower-triangular factor in w.L.
+hipError_t solve_lower(int ba, int bb, const RidgeWs& w, int h, int L, hipStream_t s) {
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
+  const int r0 = blk_row(ba, h), r2 = blk_row(bb, h);
+  if (bb - ba == 1) {
+    float* rk = w.R + static_cast<int64_t>(r0) * h;
+    const float* linv = w.Linv + static_cast<int64_t>(r0) * kCholBlock;
+    const int nbk = r2 - r0;
+    return gemm(nbk, h, nbk, linv, kCholBlock, 1, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
+                0.f, L, false, s);
+  }
+  const int bm = (ba + bb) / 2, r1 = blk_row(bm, h);
+  hipError_t e = solve_lower(ba, bm, w, h, L, s);
+  if (e != hipSuccess) return e;
+  // R[r1:r2] -= L[r1:r2, r0:r1] R[r0:r1]
+  e = gemm(r2 - r1, h, r1 - r0, w.L + static_cast<int64_t>(r1) * h + r0, h, 1, hh, false,
+           w.R + static_cast<int64_t>(r0) * h, h, 1, hh, false, w.R + static_cast<int64_t>(r1) * h,
+           h, hh, -1.f, 1.f, L, false, s);
+  if (e != hipSuccess) return e;
+  return solve_lower(bm, bb, w, h, L, s);
+}
+
+// R[rows of blocks ba..bb) <- L^-T R.
+hipError_t solve_upper(int ba, int bb, const RidgeWs& w, int h, int L, hipStream_t s) {
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
+  const int r0 = blk_row(ba, h), r2 = blk_row(bb, h);
+  if (bb - ba == 1) {
+    float* rk = w.R + static_cast<int64_t>(r0) * h;
+    const float* linv = w.Linv + static_cast<int64_t>(r0) * kCholBlock;
+    const int nbk = r2 - r0;
+    return gemm(nbk, h, nbk, linv, 1, kCholBlock, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
+                0.f, L, false, s);
+  }
+  const int bm = (ba + bb) / 2, r1 = blk_row(bm, h);
+  hipError_t e = solve_upper(bm, bb, w, h, L, s);
+  if (e != hipSuccess) return e;
+  // R[r0:r1] -= L[r1:r2, r0:r1]^T R[r1:r2]
+  e = gemm(r1 - r0, h, r2 - r1, w.L + static_cast<int64_t>(r1) * h + r0, 1, h, hh, false,
+           w.R + static_cast<int64_t>(r1) * h, h, 1, hh, false, w.R + static_cast<int64_t>(r0) * h,
+           h, hh, -1.f, 1.f, L, false, s);
+  if (e != hipSuccess) return e;
+  return solve_upper(ba, bm, w, h, L, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,35 +251,14 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const 
                 s));
   ISPA_TRY(ispa::launch_transpose(w.R, w.Bt, h, L, s));
 
-  // Forward substitution L Z = R, block rows top to bottom.
-  for (int kb = 0; kb < nblk; ++kb) {
-    const int k0 = kb * kCholBlock;
-    const int nbk = (h - k0) < kCholBlock ? (h - k0) : kCholBlock;
-    const int rem = h - k0 - nbk;
-    float* rk = w.R + static_cast<int64_t>(k0) * h;
-    const float* linv = w.Linv + static_cast<int64_t>(k0) * kCholBlock;
-    ISPA_TRY(gemm(nbk, h, nbk, linv, kCholBlock, 1, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
-                  0.f, L, false, s));
-    if (rem > 0) {
-      ISPA_TRY(gemm(rem, h, nbk, w.L + static_cast<int64_t>(k0 + nbk) * h + k0, h, 1, hh, false,
-                    rk, h, 1, hh, false, rk + static_cast<int64_t>(nbk) * h, h, hh, -1.f, 1.f, L,
-                    false, s));
-    }
-  }
-  // Back substitution L^T dW = Z, block rows bottom to top.
-  for (int kb = nblk - 1; kb >= 0; --kb) {
-    const int k0 = kb * kCholBlock;
-    const int nbk = (h - k0) < kCholBlock ? (h - k0) : kCholBlock;
-    float* rk = w.R + static_cast<int64_t>(k0) * h;
-    const float* linv = w.Linv + static_cast<int64_t>(k0) * kCholBlock;
-    ISPA_TRY(gemm(nbk, h, nbk, linv, 1, kCholBlock, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
-                  0.f, L, false, s));
-    if (k0 > 0) {
-      // R[0:k0] -= L[k0:k0+nbk, 0:k0]^T X_k
-      ISPA_TRY(gemm(k0, h, nbk, w.L + static_cast<int64_t>(k0) * h, 1, h, hh, false, rk, h, 1, hh,
-                    false, w.R, h, hh, -1.f, 1.f, L, false, s));
-    }
-  }
+  // Forward substitution L Z = R, then back substitution L^T X = Z, both by
+  // recursive halving over the 128-row blocks: solve one half, update the
+  // other half with one large GEMM (K up to h/2), solve it. The leaves apply
+  // the diagonal-block inverses in place. Compared with block-row sweeps this
+  // touches each row of R O(log(h/128)) times instead of O(h/128) times, and
+  // the update GEMMs are large.
+  ISPA_TRY(solve_lower(0, nblk, w, h, L, s));
+  ISPA_TRY(solve_upper(0, nblk, w, h, L, s));
   ISPA_TRY(ispa::launch_transpose(w.R, dW, h, L, s));
   return ISPA_OK;
 }
