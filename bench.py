@@ -546,7 +546,7 @@ def main():
         "attn_ms_per_step": round(attn_ms, 3),
         "dW_absorb_ms_per_layer": round(absorb_ms / w.n_layers, 3),
         "absorb_ms_per_step": round(absorb_ms, 3),
-        "absorb_fp32_tflops": round(absorb_tflops, 2),
+        "absorb_tflops": round(absorb_tflops, 2),
         "gram_tflops": round(gram_tflops, 2),
         "gram_pct_bf16_peak": round(100 * gram_tflops / PEAK_BF16_TFLOPS, 2),
         "gram_ms_per_step": round(tot["gram"] / K, 3),

@@ -3,7 +3,8 @@
 // Gram accumulation (ISPA paper §3.1 item 2: the accumulated dual-stream
 // activations are the basis of the weight adaption): for X = O_local and
 // D = O_full - O_local of one warmup step, G += X^T X, C += X^T D, E += D^T D,
-// in fp32. Treating Y = [X | D] as one [n_tok, 2h] matrix, every needed block
+// in fp32. Without D (G-only mode) the same kernel forms X^T X alone; the
+// layer score uses it for W_o^T W_o. Treating Y = [X | D] as one [n_tok, 2h] matrix, every needed block
 // is a 128 x 128 tile (bi <= bj) of the symmetric Y^T Y: both-X tiles feed G,
 // X-D tiles feed C, both-D tiles feed E. Off-diagonal tiles of G and E are
 // also added, transposed, into the mirror tile so G and E stay exactly
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
   // panels are fetched once into that XCD's L2 and shared, instead of every
   // tile streaming its own column panel.
   int idx = xcd_remap(blockIdx.x, n_tiles);
-  const int nb2 = 2 * nbp;
+  const int nb2 = p.d ? 2 * nbp : nbp;  // without D only the X X^T blocks (G)
   const int ng = (nb2 + kGroup - 1) / kGroup;
   int bi = 0, bj = 0;
   for (int gi = 0; gi < ng; ++gi) {
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
   const int h = p.h;
   const int64_t hh = static_cast<int64_t>(h) * h;
   const uint16_t* xb = p.x + b * p.n_tok * h;
-  const uint16_t* db = p.d + b * p.n_tok * h;
+  const uint16_t* db = p.d ? p.d + b * p.n_tok * h : xb;
   const bool i_is_d = bi >= nbp, j_is_d = bj >= nbp;
   const int fi0 = (i_is_d ? bi - nbp : bi) * kT;
   const int fj0 = (j_is_d ? bj - nbp : bj) * kT;
@@ -262,10 +263,16 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
 constexpr int kPK = 32;           // k per stage (projection)
 constexpr int kPStr = kPK + 8;    // LDS row stride (bf16)
 
-__global__ __launch_bounds__(kThreads, 2) void project_kernel(const uint16_t* __restrict__ x,
-                                                               const uint16_t* __restrict__ w,
-                                                               uint16_t* __restrict__ y,
-                                                               int64_t n, int h_in, int h_out) {
+// NT GEMM on bf16 matrix cores, fp32 accumulate: Y[m][o] = sum_k A[m][k] W[o][k]
+// (both operands k-contiguous), batched over blockIdx.y. F32OUT = false: Y is
+// bf16 (the projection). F32OUT = true: Y is fp32 and, when a2 is given, the
+// A operand is a + a2 (two bf16 planes of an fp32 matrix: the contraction
+// runs over both with the same W), i.e. an fp32 x bf16 product.
+template <bool F32OUT>
+__global__ __launch_bounds__(kThreads, 2) void nt_gemm_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ a2, int64_t a_bs,
+    const uint16_t* __restrict__ w, int64_t w_bs, void* __restrict__ yv, int64_t y_bs, int64_t n,
+    int h_in, int h_out) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[2][kT * kPStr];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][kT * kPStr];
   const int tid = threadIdx.x;
@@ -275,20 +282,24 @@ __global__ __launch_bounds__(kThreads, 2) void project_kernel(const uint16_t* __
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t m0 = static_cast<int64_t>(t / tiles_n) * kT;
   const int n0 = (t % tiles_n) * kT;
+  const int64_t b = blockIdx.y;
+  const uint16_t* x = a + b * a_bs;
+  const uint16_t* x2 = a2 ? a2 + b * a_bs : nullptr;
+  const uint16_t* wb = w + b * w_bs;
 
   // thread -> (row, 16-byte chunk): 128 rows x 4 chunks, 2 per thread
   uint4 ra[2], rb[2];
-  auto load = [&](int k0) {
+  auto load = [&](const uint16_t* xs, int k0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int u = tid + q * kThreads;
       const int row = u / 4, c = u % 4;
       const int k = k0 + 8 * c;
       ra[q] = (m0 + row < n && k < h_in)
-                  ? *reinterpret_cast<const uint4*>(x + (m0 + row) * h_in + k)
+                  ? *reinterpret_cast<const uint4*>(xs + (m0 + row) * h_in + k)
                   : make_uint4(0, 0, 0, 0);
       rb[q] = (n0 + row < h_out && k < h_in)
-                  ? *reinterpret_cast<const uint4*>(w + static_cast<int64_t>(n0 + row) * h_in + k)
+                  ? *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(n0 + row) * h_in + k)
                   : make_uint4(0, 0, 0, 0);
     }
   };
@@ -308,21 +319,36 @@ __global__ __launch_bounds__(kThreads, 2) void project_kernel(const uint16_t* __
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  const int nst = (h_in + kPK - 1) / kPK;
-  load(0);
+  const int nk = (h_in + kPK - 1) / kPK;
+  const int nst = x2 ? 2 * nk : nk;  // stage s < nk: plane a; s >= nk: plane a2
+  auto stage_src = [&](int s, const uint16_t*& xs, int& k0) {
+    xs = s < nk ? x : x2;
+    k0 = (s < nk ? s : s - nk) * kPK;
+  };
+  {
+    const uint16_t* xs;
+    int k0;
+    stage_src(0, xs, k0);
+    load(xs, k0);
+  }
   store(0);
   __syncthreads();
   for (int s = 0; s < nst; ++s) {
     const int buf = s & 1;
     const bool has_next = s + 1 < nst;
-    if (has_next) load((s + 1) * kPK);
+    if (has_next) {
+      const uint16_t* xs;
+      int k0;
+      stage_src(s + 1, xs, k0);
+      load(xs, k0);
+    }
 #pragma unroll
     for (int kk = 0; kk < kPK / 16; ++kk) {
-      bf16x8 a[2], bb[2];
+      bf16x8 av[2], bb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(sa[buf] + (wm * 64 + i * 32 + l32) * kPStr +
-                                                16 * kk + 8 * hf);
+        av[i] = *reinterpret_cast<const bf16x8*>(sa[buf] + (wm * 64 + i * 32 + l32) * kPStr +
+                                                 16 * kk + 8 * hf);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         bb[j] = *reinterpret_cast<const bf16x8*>(sb[buf] + (wn * 64 + j * 32 + l32) * kPStr +
@@ -330,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void project_kernel(const uint16_t* __
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], bb[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(av[i], bb[j], acc[i][j]);
     }
     if (has_next) store(buf ^ 1);
     __syncthreads();
@@ -345,9 +371,26 @@ __global__ __launch_bounds__(kThreads, 2) void project_kernel(const uint16_t* __
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-        if (m < n) y[m * h_out + o] = f32_to_bf16_bits(acc[i][j][r]);
+        if (m >= n) continue;
+        if constexpr (F32OUT)
+          static_cast<float*>(yv)[b * y_bs + m * h_out + o] = acc[i][j][r];
+        else
+          static_cast<uint16_t*>(yv)[b * y_bs + m * h_out + o] = f32_to_bf16_bits(acc[i][j][r]);
       }
     }
+  }
+}
+
+// fp32 -> two bf16 planes: hi = rne(c), lo = rne(c - hi); hi + lo holds c to
+// about 2^-17 relative.
+__global__ void split_bf16_kernel(const float* __restrict__ c, uint16_t* __restrict__ hi,
+                                  uint16_t* __restrict__ lo, int64_t count) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const float v = c[i];
+    const uint16_t h = f32_to_bf16_bits(v);
+    hi[i] = h;
+    lo[i] = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
   }
 }
 
@@ -355,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 2) void project_kernel(const uint16_t* __
 
 hipError_t launch_gram(const GramParams& p, hipStream_t stream) {
   const int nbp = (p.h + kT - 1) / kT;
-  const int nb2 = 2 * nbp;
+  const int nb2 = p.d ? 2 * nbp : nbp;
   const int n_tiles = nb2 * (nb2 + 1) / 2;
   if (p.batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(gram_kernel, dim3(n_tiles, p.batch), dim3(kThreads), 0, stream, p, nbp,
@@ -367,8 +410,22 @@ hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int
                           int h_out, hipStream_t stream) {
   const int64_t tiles = ((n + kT - 1) / kT) * ((h_out + kT - 1) / kT);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(project_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
-                     stream, x, w, y, n, h_in, h_out);
+  hipLaunchKernelGGL(nt_gemm_kernel<false>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
+                     stream, x, nullptr, 0, w, 0, static_cast<void*>(y), 0, n, h_in, h_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_nt_gemm_f32(const float* c, uint16_t* hi, uint16_t* lo,
+                                    const uint16_t* w, float* y, int h, int batch,
+                                    hipStream_t stream) {
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  const int64_t count = hh * batch;
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_bf16_kernel, dim3(4096), dim3(256), 0, stream, c, hi, lo, count);
+  const int64_t tiles = static_cast<int64_t>((h + kT - 1) / kT) * ((h + kT - 1) / kT);
+  hipLaunchKernelGGL(nt_gemm_kernel<true>, dim3(static_cast<unsigned>(tiles), batch),
+                     dim3(kThreads), 0, stream, hi, lo, hh, w, hh, static_cast<void*>(y), hh,
+                     static_cast<int64_t>(h), h, h);
   return hipGetLastError();
 }
 

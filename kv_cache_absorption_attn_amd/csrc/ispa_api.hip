@@ -246,9 +246,17 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const 
     }
   }
 
-  // R = C W (math layout [in, out]); W(k, o) = Wo[o][k]. Keep (C W)^T for scoring.
-  ISPA_TRY(gemm(h, h, h, C, h, 1, hh, false, Wo, 1, h, hh, true, w.R, h, hh, 1.f, 0.f, L, false,
-                s));
+  // R = C W (math layout [in, out]); W(k, o) = Wo[o][k], i.e. R[i][o] =
+  // sum_k C[i][k] Wo[o][k]: on the bf16 matrix cores with C split into two
+  // bf16 planes (hi + lo holds C to ~2^-17 relative, about the rounding of an
+  // fp32 accumulation over k), staged in Bt, which is free until (C W)^T is
+  // written there below. Keep (C W)^T for scoring.
+  {
+    uint16_t* chi = reinterpret_cast<uint16_t*>(w.Bt);
+    uint16_t* clo = chi + static_cast<int64_t>(L) * hh;
+    ISPA_TRY(ispa::launch_split_nt_gemm_f32(C, chi, clo, static_cast<const uint16_t*>(Wo), w.R, h,
+                                            L, s));
+  }
   ISPA_TRY(ispa::launch_transpose(w.R, w.Bt, h, L, s));
 
   // Forward substitution L Z = R, then back substitution L^T X = Z, both by
@@ -279,9 +287,20 @@ int ispa_layer_score(int n_layers, int h, const float* G, const float* C, const 
   const hipStream_t s = as_stream(stream);
   const RidgeWs w = ridge_layout(workspace, n_layers, h);
   const int64_t hh = static_cast<int64_t>(h) * h;
-  // P = W W^T (math W = Wo^T): P(i, j) = sum_o Wo[o][i] Wo[o][j]; lower tiles.
-  ISPA_TRY(gemm(h, h, h, Wo, 1, h, hh, true, Wo, h, 1, hh, true, w.L, h, hh, 1.f, 0.f, n_layers,
-                true, s));
+  // P = W W^T (math W = Wo^T): P(i, j) = sum_o Wo[o][i] Wo[o][j], the Gram of
+  // the bf16 rows of Wo, formed on the bf16 matrix cores (products exact in
+  // fp32, fp32 accumulation); both triangles are written.
+  {
+    ispa::GramParams gp{};
+    gp.x = static_cast<const uint16_t*>(Wo);
+    gp.d = nullptr;
+    gp.n_tok = h;
+    gp.h = h;
+    gp.batch = n_layers;
+    gp.G = w.L;
+    gp.zero_first = 1;
+    ISPA_TRY(ispa::launch_gram(gp, s));
+  }
   ispa::ScoreParams p{};
   p.n_layers = n_layers;
   p.h = h;

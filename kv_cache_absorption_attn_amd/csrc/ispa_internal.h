@@ -33,7 +33,7 @@ int attn_q_tile_min();  // smallest query tile of any attention kernel
 // ---------------------------------------------------------------- Gram
 struct GramParams {
   const uint16_t* x;         // [batch][n_tok, h] bf16
-  const uint16_t* d;
+  const uint16_t* d;         // null: G only
   int64_t n_tok;
   int h;
   int batch;
@@ -43,6 +43,12 @@ struct GramParams {
   int zero_first;
 };
 hipError_t launch_gram(const GramParams& p, hipStream_t stream);
+// Y[b] = C[b] W[b]^T-style product in fp32: Y[b][i][o] = sum_k C[b][i][k] W[b][o][k]
+// for fp32 C (split into two bf16 planes hi, lo of [batch][h, h] each) and
+// bf16 W; bf16 matrix cores, fp32 accumulate.
+hipError_t launch_split_nt_gemm_f32(const float* c, uint16_t* hi, uint16_t* lo,
+                                    const uint16_t* w, float* y, int h, int batch,
+                                    hipStream_t stream);
 
 // ---------------------------------------------------------------- fp32 GEMM
 // C[b](m, n) = alpha * sum_k A[b](m, k) B[b](k, n) + beta * C[b](m, n)
