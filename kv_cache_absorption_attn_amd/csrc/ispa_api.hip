@@ -114,6 +114,53 @@ hipError_t solve_upper(int ba, int bb, const RidgeWs& w, int h, int L, hipStream
   return solve_upper(ba, bm, w, h, L, s);
 }
 
+// Columns of blocks [ca, cb) of the rows [x0, x1) of w.L: X <- X L^-T for the
+// lower-triangular diagonal part L[blocks ca..cb) (already factored, with the
+// diagonal-block inverses in w.Linv).
+hipError_t solve_right(int ca, int cb, int x0, int x1, const RidgeWs& w, int h, int L,
+                       hipStream_t s) {
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
+  const int c0 = blk_row(ca, h), c2 = blk_row(cb, h);
+  float* x = w.L + static_cast<int64_t>(x0) * h;
+  if (cb - ca == 1) {
+    // X_k <- X_k Linv_kk^T   (in place: one tile column)
+    const float* linv = w.Linv + static_cast<int64_t>(c0) * kCholBlock;
+    const int nbk = c2 - c0;
+    return gemm(x1 - x0, nbk, nbk, x + c0, h, 1, hh, false, linv, 1, kCholBlock, lb, false,
+                x + c0, h, hh, 1.f, 0.f, L, false, s);
+  }
+  const int cm = (ca + cb) / 2, c1 = blk_row(cm, h);
+  hipError_t e = solve_right(ca, cm, x0, x1, w, h, L, s);
+  if (e != hipSuccess) return e;
+  // X[:, c1:c2] -= X[:, c0:c1] L[c1:c2, c0:c1]^T
+  e = gemm(x1 - x0, c2 - c1, c1 - c0, x + c0, h, 1, hh, false,
+           w.L + static_cast<int64_t>(c1) * h + c0, 1, h, hh, false, x + c1, h, hh, -1.f, 1.f, L,
+           false, s);
+  if (e != hipSuccess) return e;
+  return solve_right(cm, cb, x0, x1, w, h, L, s);
+}
+
+// Cholesky factor of the diagonal blocks [ba, bb) of w.L (their trailing
+// updates from earlier columns already applied).
+hipError_t cholesky(int ba, int bb, const RidgeWs& w, int h, int L, int* info, hipStream_t s) {
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  const int r0 = blk_row(ba, h), r2 = blk_row(bb, h);
+  if (bb - ba == 1) return ispa::launch_potrf_block(w.L, w.Linv, h, r0, r2 - r0, L, info, ba == 0, s);
+  const int bm = (ba + bb) / 2, r1 = blk_row(bm, h);
+  hipError_t e = cholesky(ba, bm, w, h, L, info, s);
+  if (e != hipSuccess) return e;
+  // L21 = A21 L11^-T
+  e = solve_right(ba, bm, r1, r2, w, h, L, s);
+  if (e != hipSuccess) return e;
+  // A22 -= L21 L21^T   (lower 128-tiles only)
+  float* l21 = w.L + static_cast<int64_t>(r1) * h + r0;
+  e = gemm(r2 - r1, r2 - r1, r1 - r0, l21, h, 1, hh, false, l21, 1, h, hh, false,
+           w.L + static_cast<int64_t>(r1) * h + r1, h, hh, -1.f, 1.f, L, true, s);
+  if (e != hipSuccess) return e;
+  return cholesky(bm, bb, w, h, L, info, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,25 +273,12 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const 
   const int L = n_layers;
   const int nblk = (h + kCholBlock - 1) / kCholBlock;
 
-  // Cholesky of M = G + lambda I, one 128-column block at a time.
+  // Cholesky of M = G + lambda I by recursive halving over the 128-column
+  // blocks (leaves factor and invert one diagonal block; panels are solved
+  // against the leaves' inverses; trailing updates are single large
+  // lower-tile products).
   ISPA_TRY(ispa::launch_copy_add_diag(G, w.L, h, L, lambda, s));
-  for (int kb = 0; kb < nblk; ++kb) {
-    const int k0 = kb * kCholBlock;
-    const int nbk = (h - k0) < kCholBlock ? (h - k0) : kCholBlock;
-    const int rem = h - k0 - nbk;
-    ISPA_TRY(ispa::launch_potrf_block(w.L, w.Linv, h, k0, nbk, L, info, kb == 0, s));
-    if (rem > 0) {
-      float* panel = w.L + static_cast<int64_t>(k0 + nbk) * h + k0;
-      const float* linv = w.Linv + static_cast<int64_t>(k0) * kCholBlock;
-      // panel <- panel * Linv_kk^T   (in place: one tile column)
-      ISPA_TRY(gemm(rem, nbk, nbk, panel, h, 1, hh, false, linv, 1, kCholBlock, lb, false, panel,
-                    h, hh, 1.f, 0.f, L, false, s));
-      // trailing <- trailing - panel panel^T   (lower 128-tiles only)
-      ISPA_TRY(gemm(rem, rem, nbk, panel, h, 1, hh, false, panel, 1, h, hh, false,
-                    w.L + static_cast<int64_t>(k0 + nbk) * h + k0 + nbk, h, hh, -1.f, 1.f, L,
-                    true, s));
-    }
-  }
+  ISPA_TRY(cholesky(0, nblk, w, h, L, info, s));
 
   // R = C W (math layout [in, out]); W(k, o) = Wo[o][k], i.e. R[i][o] =
   // sum_k C[i][k] Wo[o][k]: on the bf16 matrix cores with C split into two

@@ -282,14 +282,11 @@ hipError_t launch_copy_add_diag(const float* G, float* L, int h, int batch, floa
 hipError_t launch_potrf_block(float* L, float* Linv, int h, int k0, int nb, int batch, int* info,
                               int info_first, hipStream_t stream) {
   const size_t lds = 2 * kNB * kLdsLd * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_block_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every call (cheap): no process-wide state, valid for any device
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_block_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(potrf_block_kernel, dim3(batch), dim3(256), lds, stream, L, Linv, h, k0, nb,
                      info, info_first);
   return hipGetLastError();
