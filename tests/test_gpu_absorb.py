@@ -88,7 +88,7 @@ def test_gram_tiny_warmup():
     np.testing.assert_array_equal(Eh, Eh.T)
 
 
-@pytest.mark.parametrize("n_tok,h,batch", [(100, 192, 2), (1, 64, 1), (333, 256, 3)])
+@pytest.mark.parametrize("n_tok,h,batch", [(100, 192, 2), (1, 64, 1), (333, 256, 3), (200, 512, 2)])
 def test_gram_ragged(n_tok, h, batch):
     log(f"gram ragged n={n_tok} h={h} b={batch}")
     x = wl.random_bf16((batch, n_tok, h), 0.5, 11 + h)
@@ -141,7 +141,7 @@ def _synthetic_stats(L, h, n, seed):
     return f32(Gs), f32(Cs), f32(Es), dev_bf16(np.stack(Ws))
 
 
-@pytest.mark.parametrize("L,h,n", [(1, 128, 300), (3, 320, 500), (2, 64, 50)])
+@pytest.mark.parametrize("L,h,n", [(1, 128, 300), (3, 320, 500), (2, 64, 50), (2, 256, 400)])
 def test_ridge_and_score(L, h, n):
     log(f"ridge L={L} h={h} n={n}")
     lam = 1e-2
