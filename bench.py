@@ -309,7 +309,10 @@ def pmc_summary(fetch_csv: str, write_csv: str, w: wl.Workload):
         copy = [v for _, n, v in rows if "copyBuffer" in n and v > 1024][-1]
         attn = [v for _, n, v in rows if "attn_decomp_kernel<128>" in n]
         attn = [v for i, v in enumerate(attn) if i % (n_warm + n_post) < n_warm]
+        # each step: n_warm Gram launches of the warmup, then one G-only launch
+        # (W_o^T W_o of the layer score), which is left out
         gram = [v for _, n, v in rows if "gram_kernel" in n]
+        gram = [v for i, v in enumerate(gram) if i % (n_warm + 1) < n_warm]
         return copy, {"attn_decomp_kernel<128>": attn, "gram_kernel": gram}
 
     fc, fe = read(fetch_csv, "FETCH_SIZE")
@@ -369,6 +372,7 @@ def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
     warm = [dt for i, dt in enumerate(attn) if i % (n_warm + n_post) < n_warm]
     post = [dt for i, dt in enumerate(attn) if i % (n_warm + n_post) >= n_warm]
     gram = [dt for _, n, dt in rows if "gram_kernel" in n]
+    gram = [dt for i, dt in enumerate(gram) if i % (n_warm + 1) < n_warm]  # warmup Gram only
     n_kv = [w.n_sink + w.n_cur + hs for hs in w.hist_per_step]
     fl = sum(attn_flops(w.n_q, nk, w.hidden) for nk in n_kv) / len(n_kv)
     lines = [
