@@ -125,3 +125,20 @@ def test_wan14_headline_sampled_rows():
     """14B-class last warmup step: 40 heads, 4680 queries, 1560 + 4680 local
     keys and 56160 history keys."""
     _sampled_rows(wl.WAN14_WARMUP, 3, n_rows=32)
+
+
+def test_wan14_stream_full_only_sampled_rows():
+    """14B-class streaming chunk on an F-layer at the longest history (120 latent
+    frames: 1560 + 4680 local and 187200 history keys, 40 heads): only O_full and
+    LSE_full are requested, i.e. the single-pass full-only path, at its real size;
+    sampled rows against full attention over the concatenated KV."""
+    w = wl.WAN14_STREAM
+    st = wl.step_inputs(w, 0, 0)
+    log(f"attn 14B stream full-only: n_q={st.q.shape[0]} hist={st.k_hist.shape[0]}")
+    gpu, _ = run_attention(st, w.sm_scale, outputs=("o_full", "lse_full"))
+    rows = np.sort(np.random.default_rng(5).choice(st.q.shape[0], 32, replace=False))
+    k_all = np.concatenate([st.k_sink, st.k_cur, st.k_hist])
+    v_all = np.concatenate([st.v_sink, st.v_cur, st.v_hist])
+    o_ref, lse_ref = orc.multihead_attention(st.q[rows], k_all, v_all, w.sm_scale)
+    compare_attention({"o_full": gpu["o_full"][rows], "lse_full": gpu["lse_full"][:, rows]},
+                      {"o_full": o_ref, "lse_full": lse_ref})

@@ -96,6 +96,13 @@ WAN14_WARMUP = Workload("wan14b_warmup", 3, 40, 40, 128, _frames(3),
                         tuple(_frames(12 * s) for s in range(4)), 1e-2, 20,
                         1.0, 1.0 / math.sqrt(5120.0), True)
 
+# 14B-class long-horizon streaming after absorption: one chunk at the longest
+# history of the run, 120 latent frames (the F-layers attend all of it). Used
+# for sampled-row parity of the full-only pass; the streaming timing draws its
+# own device-side inputs.
+WAN14_STREAM = Workload("wan14b_stream", 4, 40, 40, 128, _frames(3), _frames(1), _frames(3),
+                        (_frames(120),), 1e-2, 20, 1.0, 1.0 / math.sqrt(5120.0), True)
+
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
                                   (TINY, TINY_1HEAD, WAN13_LAYER, WAN13_WARMUP,
                                    WAN14_WARMUP)}
