@@ -31,8 +31,10 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
-# Per-source extra flags.
-EXTRA: dict = {}
+# Per-source extra flags. The attention kernel takes its inputs as finite:
+# without NaN semantics fmax needs no operand canonicalisation, which removes
+# about one vector instruction in ten from the softmax.
+EXTRA: dict = {"attn_decomp.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

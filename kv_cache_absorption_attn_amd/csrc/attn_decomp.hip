@@ -12,18 +12,22 @@
 // Work decomposition: one workgroup = one head x 256 queries, 8 waves in 4
 // pairs of 64 queries (two 32-query blocks). In a pair the S-wave computes
 // the scores and the online softmax, the O-wave accumulates the output one
-// tile behind it; both run on one SIMD. A mid-step barrier holds the O-wave's
-// PV until the S-wave has issued its K Q^T, so the PV runs during the
-// softmax (vector ALU) rather than against the K Q^T (matrix cores). K/V stream through LDS
-// in 64-key tiles (double buffered, one barrier per tile). Per tile and pair:
-//   S-wave: S^T[64 keys x 64 queries] = K Q^T   (32 MFMA 32x32x16, K from LDS
-//           with 16-byte reads, Q^T in registers), then the online softmax on
-//           S^T (each lane owns one query per block: in-lane reductions plus
-//           one exchange between the lane halves), then P^T to LDS in the
-//           MFMA operand layout, with the rescale factors of any move of the
-//           running max.
-//   O-wave: O^T[d x 64 queries] = alpha O^T + V^T P^T   (32 MFMA, V^T by
-//           transposing LDS reads, P^T by 16-byte reads)
+// tile behind it; both run on one SIMD. K/V stream through LDS in 64-key
+// tiles (double buffered, one barrier per tile); the O-wave issues every
+// tile load (V of its own tile, K two tiles ahead), so the S-wave, which
+// carries the vector work, never waits on the memory pipeline. Per tile and
+// pair:
+//   S-wave: the online softmax of tile j on S^T (each lane owns one query per
+//           block: in-lane reductions plus one exchange between the lane
+//           halves), P^T to LDS in the MFMA operand layout with the rescale
+//           factors of any move of the running max, interleaved slice by
+//           slice with S^T[64 keys x 64 queries] = K Q^T of tile j+1
+//           (32 MFMA 32x32x16, K from LDS with 16-byte reads, Q^T in
+//           registers), so the vector work runs while the matrix cores are
+//           busy.
+//   O-wave: O^T[d x 64 queries] = alpha O^T + V^T P^T of tile j-1 (32 MFMA,
+//           V^T by transposing LDS reads several MFMAs ahead, P^T by 16-byte
+//           reads)
 // Each K and V fragment read from LDS feeds two MFMAs (both query blocks).
 // The key order inside V^T is permuted so that the keys a lane holds in its
 // S^T registers are exactly the k-slots of the P^T operand.
@@ -69,19 +73,22 @@ struct TileLoader {
   static constexpr int RPI = 64 / CPR;         // rows per wave instruction
   static constexpr int IPW = kKTile / RPI / NW; // instructions per wave per tensor
   uint32_t off[IPW];                           // bytes, full tile
-  int row[IPW];                                // tile row of the lane's chunk
-  int col[IPW];                                // head * D + 8 * chunk (elements)
-  int lds_base;                                // elements
+  int w, head, lds_base;                       // lds_base in elements
 
-  // `w` in [0, NW): this wave's share of the tile rows
-  __device__ void init(int64_t rs, int head, int w, int lane) {
+  // tile row and global column (elements) of the lane's chunk in instruction i
+  __device__ int row_of(int i, int lane) const { return (w * IPW + i) * RPI + lane / CPR; }
+  __device__ int col_of(int i, int lane) const {
+    return head * D + 8 * ((lane % CPR) ^ swz<D>(row_of(i, lane)));
+  }
+
+  // `w_` in [0, NW): this wave's share of the tile rows (wave-uniform)
+  __device__ void init(int64_t rs, int head_, int w_, int lane) {
+    w = w_;
+    head = head_;
     lds_base = w * IPW * RPI * D;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      row[i] = (w * IPW + i) * RPI + lane / CPR;
-      col[i] = head * D + 8 * ((lane % CPR) ^ swz<D>(row[i]));
-      off[i] = static_cast<uint32_t>((row[i] * rs + col[i]) * 2);
-    }
+    for (int i = 0; i < IPW; ++i)
+      off[i] = static_cast<uint32_t>((row_of(i, lane) * rs + col_of(i, lane)) * 2);
   }
 
   // Loads this wave's rows of one tile of K (issue_k) or V (issue_v).
@@ -95,22 +102,30 @@ struct TileLoader {
   }
   __device__ void issue(const uint16_t* src, int64_t row0, int valid, int64_t rs,
                         uint16_t* dst) const {
-    const char* b = reinterpret_cast<const char*>(src + row0 * rs);
+    const auto res = raw_rsrc(src + row0 * rs);
     if (valid == kKTile) {
 #pragma unroll
-      for (int i = 0; i < IPW; ++i)
-        __builtin_amdgcn_global_load_lds(b + off[i], ISPA_LDS(void, dst + lds_base + i * RPI * D),
-                                         16, 0, 0);
+      for (int i = 0; i < IPW; ++i) lds_dma16(res, dst + lds_base + i * RPI * D, off[i]);
     } else {
+      const int lane = __lane_id();
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
-        const int rr = row[i] < valid ? row[i] : valid - 1;
-        __builtin_amdgcn_global_load_lds(b + (rr * rs + col[i]) * 2,
-                                         ISPA_LDS(void, dst + lds_base + i * RPI * D), 16, 0, 0);
+        const int r = row_of(i, lane);
+        const int rr = r < valid ? r : valid - 1;
+        lds_dma16(res, dst + lds_base + i * RPI * D,
+                  static_cast<uint32_t>((rr * rs + col_of(i, lane)) * 2));
       }
     }
   }
 };
+
+// Three-way max in one instruction (the compiler does not always fuse the two
+// maxima of a reduction chain); the inputs are finite scores.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // 16-byte K fragment: key row r, logical chunk c.
 template <int D>
@@ -168,10 +183,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
   __shared__ __attribute__((aligned(16))) uint16_t sv1[TBUF];
   __shared__ uint4 sp0[PSLOT];                 // [pair][qb][st][lane]
   __shared__ uint4 sp1[PSLOT];
-  __shared__ float sal0[kPairs * 64];          // rescale factor per query [pair][qb*32+q]
-  __shared__ float sal1[kPairs * 64];
-  __shared__ int sfl0[kPairs];                 // any query of the pair rescaled
-  __shared__ int sfl1[kPairs];
+  __shared__ float sal0[kPairs * 128];         // rescale factor per lane [pair][hf][qb*32+q]
+  __shared__ float sal1[kPairs * 128];
   __shared__ float s_inv_loc[kPairs * 64];     // 1 / l of the local phase
   __shared__ float s_inv_fin[kPairs * 64];     // 1 / l of the history (or only) phase
   __shared__ float s_wh[kPairs * 64];          // merge weight w_H
@@ -184,11 +197,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
   const int head = work / p.n_qtiles;
   const int qt = work % p.n_qtiles;
   const int64_t rs = static_cast<int64_t>(p.n_heads) * D;
-  int64_t qi[2];
+  int qi[2];  // query rows of the two blocks (n_q < 2^31)
   bool qvalid[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    qi[qb] = static_cast<int64_t>(qt) * kQTile + pair * kPairQ + 32 * qb + l32;
+    qi[qb] = qt * kQTile + pair * kPairQ + 32 * qb + l32;
     qvalid[qb] = qi[qb] < p.n_q;
   }
 
@@ -212,19 +225,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
   };
 
   TileLoader<D, kPairs> loader;
-  loader.init(rs, head, pair, lane);
+  loader.init(rs, head, __builtin_amdgcn_readfirstlane(pair), lane);
   const int prow = pair * 64;  // this pair's entries in the per-query arrays
+  const int prow2 = pair * 128;  // and in the per-lane rescale factors
 
   if (s_role) {
     // ------------------------------------------------------------ S-wave
     // Scores, online softmax statistics and P of every tile; P^T goes to the
-    // pair's O-wave through LDS together with the rescale factors.
+    // pair's O-wave through LDS together with the rescale factors. The S-wave
+    // runs one tile ahead of its own softmax: while the vector ALU works on
+    // the scores of tile j, the matrix cores compute those of tile j+1, one
+    // MFMA between consecutive slices of the softmax.
     bf16x8 qf[2][NT];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        qf[qb][t] = qvalid[qb] ? *reinterpret_cast<const bf16x8*>(p.q + qi[qb] * rs + head * D +
+        qf[qb][t] = qvalid[qb] ? *reinterpret_cast<const bf16x8*>(p.q + static_cast<int64_t>(qi[qb]) * rs + head * D +
                                                                   16 * t + 8 * hf)
                                : bf16x8{};
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
@@ -235,128 +252,184 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
       int64_t row0;
       tile_of(0, sg, row0, valid);
       loader.issue_k(sg, row0, valid, rs, sk0);
+      if (T > 1) {
+        tile_of(1, sg, row0, valid);
+        loader.issue_k(sg, row0, valid, rs, sk1);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    auto s_step = [&](auto buf_c, int it) {
+    // S^T[key half][query block] of the even (sa) and odd (sb) tiles
+    f32x16 sa[2][2], sb[2][2];
+    {
+      bf16x8 a0 = k_frag<D>(sk0, l32, hf), a1 = k_frag<D>(sk0, 32 + l32, hf);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        bf16x8 n0, n1;
+        if (t + 1 < NT) {
+          n0 = k_frag<D>(sk0, l32, 2 * (t + 1) + hf);
+          n1 = k_frag<D>(sk0, 32 + l32, 2 * (t + 1) + hf);
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sa[0][qb] = mfma32x32x16(a0, qf[qb][t], t ? sa[0][qb] : f32x16{});
+          sa[1][qb] = mfma32x32x16(a1, qf[qb][t], t ? sa[1][qb] : f32x16{});
+        }
+        a0 = n0;
+        a1 = n1;
+      }
+    }
+    __syncthreads();  // every wave is done with K of tile 0 before tile 2 replaces it
+
+    // Softmax of one tile (scores sc) and, when QK, K Q^T of the next tile
+    // (into sn, from K in ks). Slot u holds a slice of the softmax followed
+    // by MFMA u; the scheduling barriers keep that order, so the vector work
+    // runs while the matrix cores are busy.
+    //   row max      (8 parts: query block x 4 scores of each key half)
+    //   decision     (exchange between the lane halves, lazy rescale)
+    //   exponentials (16 items: query block x key step x half)
+    // A tail tile's rows past `valid` re-load the last valid key: their
+    // scores duplicate real ones (the row maxima need no mask) and only
+    // their exponentials are dropped, in a separate instance of this code.
+    auto body = [&](auto tail_c, auto qk_c, f32x16(&sc)[2][2], f32x16(&sn)[2][2],
+                    const uint16_t* __restrict__ ks, uint4* __restrict__ sp,
+                    float* __restrict__ sal, int valid) __attribute__((always_inline)) {
+      constexpr bool TAIL = decltype(tail_c)::value;
+      constexpr bool QK = decltype(qk_c)::value;
+      constexpr int NMF = 4 * NT;           // MFMAs of one tile's K Q^T
+      constexpr int NMAX = NT >= 8 ? 4 : 2;  // slots of the row max
+      constexpr int DEC = NMAX;             // slot of the rescale decision
+      constexpr int E0 = DEC + 1;           // first slot of the exponentials
+      float mx[2], lsum[2][4];
+      bf16x8 pv;
+      // Everything lane-dependent is derived from an opaque copy of the lane
+      // index, so it is recomputed every tile instead of being hoisted out of
+      // the tile loop and kept live (registers are the binding limit here).
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int r32 = ln & 31, h2 = ln >> 5;
+      // K fragment of k-step t: row r32 (and r32 + 32), logical chunk 2t + h2,
+      // stored at chunk (2t + h2) ^ swz = 2 (t ^ (swz >> 1)) + (h2 ^ (swz & 1))
+      const int kf = r32 * D + 8 * (h2 ^ (swz<D>(r32) & 1));
+      const int kx = 16 * (swz<D>(r32) >> 1);
+      auto kfrag = [&](int t, int half) {
+        return *reinterpret_cast<const bf16x8*>(ks + kf + 32 * D * half + (kx ^ (16 * t)));
+      };
+      // operands of the two key halves, each read at the top of the slot two
+      // slots before its first MFMA (the register being reloaded was last
+      // read by the previous slot's MFMA)
+      bf16x8 f0, f1;
+      if constexpr (QK) {
+        f0 = kfrag(0, 0);
+        f1 = kfrag(0, 1);
+      }
+#pragma unroll
+      for (int u = 0; u < NMF; ++u) {
+        if constexpr (QK) {
+          const int t = u / 4;
+          if (u % 4 == 0 && u > 0) f1 = kfrag(t, 1);
+          if (u % 4 == 2 && t + 1 < NT) f0 = kfrag(t + 1, 0);
+        }
+        // row max: one chain per query block (dependent max3 issue at full
+        // rate), 8 parts of 4 scores of each key half
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          if (w * NMAX / 8 != u) continue;
+          const int qb = w / 4, part = w % 4;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float a = sc[0][qb][4 * part + k], b = sc[1][qb][4 * part + k];
+            if (part == 0 && k == 0)
+              mx[qb] = fmaxf(a, b);
+            else
+              mx[qb] = max3(mx[qb], a, b);
+          }
+          // keep the slice in its slot (pure arithmetic is otherwise free to
+          // move to its first use, which would leave the slots unbalanced and
+          // keep every input live longer)
+          asm volatile("" : "+v"(mx[qb]));
+        }
+        if (u == DEC) {
+          // running max: moved only when the tile max exceeds it by more than
+          // the threshold; the O-wave applies the same factor to its sums
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[qb]),
+                                                             __float_as_uint(mx[qb]), false, false);
+            const float mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+            const bool need = mt > m_run[qb] + kRescaleThreshold;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
+            m_run[qb] = need ? mt : m_run[qb];
+            l_run[qb] *= alpha;
+            sal[prow2 + 64 * h2 + 32 * qb + r32] = alpha;
+          }
+        }
+        // P = 2^(s * scale_log2 - m): row sums in fp32 (the LSE needs them),
+        // P^T to LDS rounded to bf16, lane-major in the MFMA operand layout
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (E0 + k * (NMF - E0) / 16 != u) continue;
+          const int qb = k / 8, st = (k / 2) % 4, h = k % 2;
+#pragma unroll
+          for (int i = 4 * h; i < 4 * h + 4; ++i) {
+            float e = __builtin_amdgcn_exp2f(
+                fmaf(sc[st / 2][qb][8 * (st % 2) + i], p.scale_log2, -m_run[qb]));
+            if constexpr (TAIL) {
+              const int key = 32 * (st / 2) + 8 * ((8 * (st % 2) + i) / 4) + 4 * h2 + (i % 4);
+              if (key >= valid) e = 0.f;
+            }
+            lsum[qb][st] = (h == 0 && i == 0) ? e : lsum[qb][st] + e;
+            pv[i] = static_cast<__bf16>(e);
+          }
+          asm volatile("" : "+v"(lsum[qb][st]));
+          if (h == 1) {
+            sp[((pair * 2 + qb) * 4 + st) * 64 + ln] = __builtin_bit_cast(uint4, pv);
+            l_run[qb] += lsum[qb][st];
+          }
+        }
+        if constexpr (QK) {
+          const int t = u / 4, kh = (u / 2) % 2, qb = u % 2;
+          sn[kh][qb] = mfma32x32x16(kh ? f1 : f0, qf[qb][t], t ? sn[kh][qb] : f32x16{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (!QK) {
+        // no next tile: its scores are never read, which the compiler cannot
+        // see; redefining them keeps them from being live across the tile loop
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) asm volatile("" : "=v"(sn[kh][qb]));
+      }
+    };
+
+    auto s_step = [&](auto buf_c, int it) __attribute__((always_inline)) {
       constexpr int BUF = decltype(buf_c)::value;
-      const uint16_t* __restrict__ ks = BUF ? sk1 : sk0;
-      uint16_t* __restrict__ nks = BUF ? sk0 : sk1;
+      const uint16_t* __restrict__ ks = BUF ? sk0 : sk1;  // K of tile it+1
       uint4* __restrict__ sp = BUF ? sp1 : sp0;
       float* __restrict__ sal = BUF ? sal1 : sal0;
-      int* __restrict__ sfl = BUF ? sfl1 : sfl0;
       if (it < T) {
         Seg sg;
         int valid;
         int64_t row0;
-        if (it + 1 < T) {
-          tile_of(it + 1, sg, row0, valid);
-          loader.issue_k(sg, row0, valid, rs, nks);
-        }
         tile_of(it, sg, row0, valid);
-
-        // S^T[key half][query block] = K Q^T
-        f32x16 sc[2][2];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) sc[kh][qb] = f32x16{};
-        // K fragments are read one k-step ahead of their MFMAs (the
-        // scheduling barriers keep the loads from being hoisted further,
-        // which would only cost registers: the O-wave on the same SIMD hides
-        // the latency)
-        bf16x8 a0 = k_frag<D>(ks, l32, hf), a1 = k_frag<D>(ks, 32 + l32, hf);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          bf16x8 n0, n1;
-          if (t + 1 < NT) {
-            n0 = k_frag<D>(ks, l32, 2 * (t + 1) + hf);
-            n1 = k_frag<D>(ks, 32 + l32, 2 * (t + 1) + hf);
-          }
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            sc[0][qb] = mfma32x32x16(a0, qf[qb][t], sc[0][qb]);
-            sc[1][qb] = mfma32x32x16(a1, qf[qb][t], sc[1][qb]);
-          }
-          a0 = n0;
-          a1 = n1;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // A tail tile's rows past `valid` re-load the last valid key: their
-        // scores duplicate real ones (the row maxima need no mask) and only
-        // their exponentials are dropped, in a separate instance of the
-        // softmax code so the common path carries no masking.
-        auto softmax = [&](auto tail_c) {
-          constexpr bool TAIL = decltype(tail_c)::value;
-          // running max: moved only when the tile max exceeds it by more than
-          // the threshold; the O-wave applies the same factor to its sums
-          bool need[2];
-          float alpha[2], mt[2];
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            // 4-way tree: short dependency chains
-            float m4[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) m4[k] = fmaxf(sc[0][qb][k], sc[1][qb][k]);
-#pragma unroll
-            for (int i = 4; i < 16; ++i) {
-              m4[i % 4] = fmaxf(m4[i % 4], sc[0][qb][i]);
-              m4[i % 4] = fmaxf(m4[i % 4], sc[1][qb][i]);
-            }
-            const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
-                                                             __float_as_uint(mx), false, false);
-            mt[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
-            need[qb] = mt[qb] > m_run[qb] + kRescaleThreshold;
-            alpha[qb] = 1.f;
-          }
-          const bool any = __any(need[0] || need[1]);
-          if (any) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              if (need[qb]) {
-                alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - mt[qb]);
-                m_run[qb] = mt[qb];
-                l_run[qb] *= alpha[qb];
-              }
-              if (hf == 0) sal[prow + 32 * qb + l32] = alpha[qb];
-            }
-          }
-          if (lane == 0) sfl[pair] = any ? 1 : 0;
-
-          // P = 2^(s * scale_log2 - m): row sums in fp32 (the LSE needs them),
-          // P^T to LDS rounded to bf16, lane-major in the MFMA operand layout.
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            float lsum4[4] = {0.f, 0.f, 0.f, 0.f};  // one partial sum per key step
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-              bf16x8 pv;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                float e = __builtin_amdgcn_exp2f(
-                    fmaf(sc[st / 2][qb][8 * (st % 2) + i], p.scale_log2, -m_run[qb]));
-                if constexpr (TAIL) {
-                  const int key = 32 * (st / 2) + 8 * ((8 * (st % 2) + i) / 4) + 4 * hf + (i % 4);
-                  if (key >= valid) e = 0.f;
-                }
-                lsum4[st] += e;
-                pv[i] = static_cast<__bf16>(e);
-              }
-              sp[((pair * 2 + qb) * 4 + st) * 64 + lane] = __builtin_bit_cast(uint4, pv);
-            }
-            l_run[qb] += (lsum4[0] + lsum4[1]) + (lsum4[2] + lsum4[3]);
-          }
+        auto run = [&](auto tail_c, auto qk_c) __attribute__((always_inline)) {
+          if constexpr (BUF == 0)
+            body(tail_c, qk_c, sa, sb, ks, sp, sal, valid);
+          else
+            body(tail_c, qk_c, sb, sa, ks, sp, sal, valid);
         };
-        // the O-wave starts its PV only now, so its matrix work overlaps the
-        // softmax below instead of competing with the K Q^T above
-        __builtin_amdgcn_s_barrier();
-        if (valid == kKTile) {
-          softmax(std::false_type{});
+        if (it + 1 < T) {
+          if (valid == kKTile)
+            run(std::false_type{}, std::true_type{});
+          else
+            run(std::true_type{}, std::true_type{});
         } else {
-          asm volatile("" ::: "memory");
-          softmax(std::true_type{});
+          if (valid == kKTile)
+            run(std::false_type{}, std::false_type{});
+          else
+            run(std::true_type{}, std::false_type{});
         }
 
         if (split && it == n_local_tiles - 1) {
@@ -372,7 +445,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
           }
         }
       } else {
-        __builtin_amdgcn_s_barrier();
         // after the last tile: final statistics for the O-wave's epilogue
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -430,52 +502,63 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
   // parked X has been read back). With none of them requested, no merge is
   // formed and X is not needed.
   uint16_t* const park = p.o_local ? p.o_local : (p.o_full ? p.o_full : p.d_out);
-  __syncthreads();  // K of tile 0 staged (the S-waves' prologue)
+  TrOff voff[NB];  // lane offsets of the V^T operand reads, per 32-wide d block
+#pragma unroll
+  for (int b = 0; b < NB; ++b) voff[b] = tr_offsets<D>(32 * b, lane);
+  __syncthreads();  // K of tiles 0 and 1 staged (the S-waves' prologue)
+  __syncthreads();  // K Q^T of tile 0 issued
 
   auto o_step = [&](auto buf_c, int it) {
     constexpr int BUF = decltype(buf_c)::value;
     const uint16_t* __restrict__ vs = BUF ? sv0 : sv1;   // V of tile it-1
     uint16_t* __restrict__ nvs = BUF ? sv1 : sv0;        // V of tile it
+    uint16_t* __restrict__ nks = BUF ? sk1 : sk0;        // K of tile it+2
     const uint4* __restrict__ sp = BUF ? sp0 : sp1;      // P of tile it-1
     const float* __restrict__ sal = BUF ? sal0 : sal1;
-    const int* __restrict__ sfl = BUF ? sfl0 : sfl1;
     if (it < T) {
       Seg sg;
       int valid;
       int64_t row0;
       tile_of(it, sg, row0, valid);
       loader.issue_v(sg, row0, valid, rs, nvs);
+      if (it + 2 < T) {
+        tile_of(it + 2, sg, row0, valid);
+        loader.issue_k(sg, row0, valid, rs, nks);
+      }
     }
-    __builtin_amdgcn_s_barrier();  // the S-wave has issued its K Q^T
     if (it >= 1) {
       const int jb = it - 1;
-      if (__builtin_amdgcn_readfirstlane(sfl[pair])) {
+      const float al0 = sal[prow2 + 64 * hf + l32], al1 = sal[prow2 + 64 * hf + 32 + l32];
+      if (__any(al0 != 1.f || al1 != 1.f)) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const float a = sal[prow + 32 * qb + l32];
-#pragma unroll
-          for (int b = 0; b < NB; ++b) oacc[qb][b] *= a;
+        for (int b = 0; b < NB; ++b) {
+          oacc[0][b] *= al0;
+          oacc[1][b] *= al1;
         }
       }
-      // V^T operands one step ahead of their MFMAs, P^T operands one key
-      // step ahead (bounded by scheduling barriers, as in the S-wave)
+      // V^T operands PD MFMA pairs ahead of their use (the LDS latency is
+      // several MFMA pairs long), P^T operands one key step ahead
+      constexpr int NU = 4 * NB;  // u = key step * NB + d block
+      constexpr int PD = 3;
       auto pfrag = [&](int qb, int st) {
         return __builtin_bit_cast(bf16x8, sp[((pair * 2 + qb) * 4 + st) * 64 + lane]);
       };
-      bf16x8 p0 = pfrag(0, 0), p1 = pfrag(1, 0);
-      bf16x8 va = tr_operand<D>(vs, 0, 0, lane);
+      auto vfrag = [&](int u) { return tr_operand_at<D>(vs, 16 * (u / NB), voff[u % NB]); };
+      bf16x8 vq[PD];
 #pragma unroll
-      for (int u = 0; u < 4 * NB; ++u) {
+      for (int i = 0; i < PD; ++i) vq[i] = vfrag(i);
+      bf16x8 p0 = pfrag(0, 0), p1 = pfrag(1, 0), q0, q1;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
         const int st = u / NB, db = u % NB;
-        bf16x8 vn, q0, q1;
-        if (u + 1 < 4 * NB) vn = tr_operand<D>(vs, 16 * ((u + 1) / NB), 32 * ((u + 1) % NB), lane);
+        const bf16x8 va = vq[u % PD];
+        if (u + PD < NU) vq[u % PD] = vfrag(u + PD);
         if (db == 0 && st + 1 < 4) {
           q0 = pfrag(0, st + 1);
           q1 = pfrag(1, st + 1);
         }
         oacc[0][db] = mfma32x32x16(va, p0, oacc[0][db]);
         oacc[1][db] = mfma32x32x16(va, p1, oacc[1][db]);
-        va = vn;
         if (db == NB - 1) {
           p0 = q0;
           p1 = q1;

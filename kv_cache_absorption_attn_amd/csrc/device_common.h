@@ -122,6 +122,22 @@ __device__ __forceinline__ bf16x8 tr_operand_at(const uint16_t* base, int row0, 
                                  __builtin_bit_cast(bf16x4_local, hi), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Buffer resource for raw (untyped) loads from `base` with no practical range
+// limit (callers issue in-bounds offsets only); the dword-3 value selects a
+// 32-bit data format, without which untyped loads on this family read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+// Direct-to-LDS 16-byte load: lane l's 16 bytes at byte offset `voff` from the
+// resource base land at lds + 16 l. The buffer form is used rather than the
+// global one: the compiler books a global LDS load as an LDS access of unknown
+// order, after which every wait for an LDS read becomes a wait for all of
+// them (lgkmcnt(0)), which defeats reading MFMA operands ahead.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ISPA_LDS(void, lds), 16, voff, 0, 0, 0);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X. Remap
 // the hardware block id so that consecutive logical work items land on the
 // same XCD (and share its L2): logical id = start(xcd) + bid / 8.
