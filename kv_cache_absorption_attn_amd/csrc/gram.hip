@@ -48,21 +48,20 @@ struct GramLoader {
   }
   // A full stage: a uniform base plus the fixed lane offsets.
   __device__ void issue(const uint16_t* src, int h, int64_t t0, uint16_t* dst, int wave) const {
-    const char* b = reinterpret_cast<const char*>(src + t0 * h);
+    const auto res = raw_rsrc(src + t0 * h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(b + off[i]),
-                                       ISPA_LDS(void, dst + (wave * 4 + i) * 4 * kT), 16, 0, 0);
+    for (int i = 0; i < 4; ++i) lds_dma16(res, dst + (wave * 4 + i) * 4 * kT, off[i]);
   }
   // The last (partial) stage: token rows past n_tok re-load the last token.
   __device__ void issue_tail(const uint16_t* src, int h, int64_t t0, int64_t n_tok, uint16_t* dst,
                              int wave) const {
+    const auto res = raw_rsrc(src + t0 * h);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int64_t t = t0 + row[i];
       if (t >= n_tok) t = n_tok - 1;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + t * h + col[i]),
-                                       ISPA_LDS(void, dst + (wave * 4 + i) * 4 * kT), 16, 0, 0);
+      lds_dma16(res, dst + (wave * 4 + i) * 4 * kT,
+                static_cast<uint32_t>(((t - t0) * h + col[i]) * 2));
     }
   }
 };
@@ -185,17 +184,34 @@ __global__ __launch_bounds__(kThreads, 2) void gram_kernel(const GramParams p, i
                    uint16_t* __restrict__ na, uint16_t* __restrict__ nb) {
     const bool has_next = s + 1 < nst;
     if (has_next) issue_stage(s + 1, na, nb);
+    // operands of the next 16 tokens are read while this step's MFMAs run
+    bf16x8 a[2], bv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = tr_operand_at<kT>(ra, 0, oa[i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bv[j] = tr_operand_at<kT>(rb, 0, ob[j]);
 #pragma unroll
     for (int st = 0; st < kTok / 16; ++st) {
-      bf16x8 a[2], bv[2];
+      bf16x8 na[2], nbv[2];
+      if (st + 1 < kTok / 16) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = tr_operand_at<kT>(ra, 16 * st, oa[i]);
+        for (int i = 0; i < 2; ++i) na[i] = tr_operand_at<kT>(ra, 16 * (st + 1), oa[i]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bv[j] = tr_operand_at<kT>(rb, 16 * st, ob[j]);
+        for (int j = 0; j < 2; ++j) nbv[j] = tr_operand_at<kT>(rb, 16 * (st + 1), ob[j]);
+      }
+      // keeps the reads above the MFMAs (the scheduler would otherwise sink
+      // them next to their use)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], bv[j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = na[i];
+        bv[i] = nbv[i];
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
