@@ -413,10 +413,10 @@ __global__ void split_bf16_kernel(const float* __restrict__ c, uint16_t* __restr
 }  // namespace
 
 hipError_t launch_gram(const GramParams& p, hipStream_t stream) {
+  if (p.batch <= 0) return hipSuccess;
   const int nbp = (p.h + kT - 1) / kT;
   const int nb2 = p.d ? 2 * nbp : nbp;
   const int n_tiles = nb2 * (nb2 + 1) / 2;
-  if (p.batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(gram_kernel, dim3(n_tiles, p.batch), dim3(kThreads), 0, stream, p, nbp,
                      n_tiles);
   return hipGetLastError();

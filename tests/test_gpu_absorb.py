@@ -124,6 +124,55 @@ def test_gram_without_e_and_deterministic():
     assert relfro(outs[0][0], g) <= GRAM_REL and relfro(outs[0][1], c) <= GRAM_REL
 
 
+@pytest.mark.parametrize("n_tok,h,batch,with_e", [(200, 5120, 1, True), (130, 1024, 16, False)])
+def test_gram_hidden_5120_and_batched(n_tok, h, batch, with_e):
+    """Production shapes: the 14B hidden size (h = 5120, 3240 output tiles)
+    with a ragged last stage (200 = 3 x 64 + 8 tokens), and a batched case
+    without E; two accumulating calls."""
+    log(f"gram n={n_tok} h={h} b={batch} E={with_e}")
+    x = wl.random_bf16((batch, n_tok, h), 0.5, 41 + h)
+    d = wl.random_bf16((batch, n_tok, h), 0.2, 42 + h)
+    xg, dg = dev_bf16(x), dev_bf16(d)
+    G = torch.full((batch, h, h), float("nan"), dtype=torch.float32, device="cuda")
+    C = torch.full_like(G, float("nan"))
+    E = torch.full_like(G, float("nan")) if with_e else None
+    ispa.ispa_gram_accumulate(xg, dg, G, C, E, zero_first=True)
+    ispa.ispa_gram_accumulate(xg, dg, G, C, E)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        g, c, e = orc.gram_statistics([x[b], x[b]], [d[b], d[b]])
+        Gh = host(G[b])
+        assert relfro(Gh, g) <= GRAM_REL
+        assert relfro(host(C[b]), c) <= GRAM_REL
+        if with_e:
+            assert relfro(host(E[b]), e) <= GRAM_REL
+            np.testing.assert_array_equal(host(E[b]), host(E[b]).T)
+        np.testing.assert_array_equal(Gh, Gh.T)
+
+
+def test_score_hidden_5120():
+    """Layer score at the 14B hidden size over 3 layers (W_o^T W_o by the
+    G-only Gram launch batched over layers). Statistics, solve and score on
+    the GPU; the error is checked against the oracle's formula on the GPU's
+    G, C, E and dW."""
+    L, h, n, lam = 3, 5120, 200, 1e-2
+    log("score h=5120")
+    x = wl.random_bf16((L, n, h), 0.3, 51)
+    d = wl.random_bf16((L, n, h), 0.1, 52)
+    G = torch.empty((L, h, h), dtype=torch.float32, device="cuda")
+    C, E = torch.empty_like(G), torch.empty_like(G)
+    ispa.ispa_gram_accumulate(dev_bf16(x), dev_bf16(d), G, C, E, zero_first=True)
+    Wo = dev_bf16(wl.random_bf16((L, h, h), 1.0 / np.sqrt(h), 53))
+    dW, info, ws = ridge_gpu(G, C, Wo, lam)
+    assert np.all(info.cpu().numpy() == 0)
+    ea, er, sel = score_gpu(G, C, E, Wo, dW, lam, info, 1, ws)
+    for l in range(L):
+        ref = orc.layer_error_from_stats(host(G[l]), host(C[l]), host(E[l]), host(Wo[l]),
+                                         host(dW[l]), lam)
+        log(f"  layer {l}: eps_rel {er[l]:.6e} oracle {ref[1]:.6e}")
+        assert abs(er[l] - ref[1]) <= eps_tol(ref[1], h), (er[l], ref)
+
+
 # ------------------------------------------------------------------ ridge + score
 
 def _synthetic_stats(L, h, n, seed):
