@@ -307,3 +307,35 @@ def run_warmup_layer(steps, wo, lam: float, scale: float):
     return {"x_all": np.concatenate(xs), "z_all": np.concatenate(zs),
             "d_all": np.concatenate(ds), "g": g, "c": c, "e": e, "dw": dw,
             "eps_abs": eps_abs, "eps_rel": eps_rel}
+
+
+# ---------------------------------------------------------------------------
+# Streaming after the transition (ISPA paper §3.1 item 3 and §3.3: the K
+# selected layers take W + dW and permanently drop their history KV, so they
+# attend the sink and current tokens only; the other layers keep attending
+# the whole history through the original W)
+# ---------------------------------------------------------------------------
+
+def history_chunks(c: int, capacity_chunks: Optional[int] = None) -> list:
+    """Indices of the earlier chunks that a full-history layer attends while
+    chunk c (0-based, counted from the first chunk the cache saw) is
+    current. The paper keeps the whole history (capacity None); a finite
+    capacity keeps the `capacity_chunks` most recent chunks, dropping the
+    oldest first."""
+    lo = 0 if capacity_chunks is None else max(0, c - capacity_chunks)
+    return list(range(lo, c))
+
+
+def stream_layer_chunk(q, k_sink, v_sink, k_chunks, v_chunks, c: int, wo,
+                       scale: float, *, local_only: bool,
+                       capacity_chunks: Optional[int] = None):
+    """One layer while chunk c is current. k_chunks / v_chunks hold the
+    [n_cur, nh, d] keys / values of chunks 0..c in order (chunk c is the
+    current one). An L-layer (local_only) attends sink + current; an F-layer
+    attends sink + its history chunks + current, the keys concatenated in
+    time order. Returns (O [nq, h], Y = O wo^T)."""
+    hist = [] if local_only else history_chunks(c, capacity_chunks)
+    k = np.concatenate([k_sink] + [k_chunks[i] for i in hist] + [k_chunks[c]], axis=0)
+    v = np.concatenate([v_sink] + [v_chunks[i] for i in hist] + [v_chunks[c]], axis=0)
+    o, _ = multihead_attention(q, k, v, scale)
+    return o, project(o, wo)
