@@ -15,7 +15,9 @@
  *
  * Conventions for every entry point:
  *  - Pointers are device pointers unless stated otherwise; the caller owns
- *    every buffer. The library never allocates, frees or synchronises.
+ *    every buffer. The library never allocates, frees or synchronises, with
+ *    the one exception of the streaming KV cache (ispa_kv_*), which owns the
+ *    KV memory it manages.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and the call returns immediately. Argument checks are synchronous: on
  *    any error status nothing has been enqueued.
@@ -45,7 +47,7 @@ enum {
   ISPA_ERR_UNSUPPORTED = 3, /* a valid but unsupported configuration */
   ISPA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ISPA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
-  ISPA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+  ISPA_ERR_HIP = 6          /* the HIP runtime reported an error (launch, copy, mapping) */
 };
 
 /* Static text for a status code (never NULL). */
@@ -177,6 +179,139 @@ int ispa_apply_dW(int n_layers, int h, const int* selected, const float* dW,
  */
 int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in,
                  int h_out, void* stream);
+
+/*
+ * ------------------------------------------------------------------------
+ * Streaming KV cache and the per-layer streaming step (§3.1 item 3 and
+ * §3.3: after the transition the K selected layers (L-layers) attend the
+ * sink and current tokens only, through W + dW, and drop their history KV
+ * for good; the other layers (F-layers) keep attending their whole history
+ * through W).
+ *
+ * One cache holds, for each of n_layers layers, the K and V rows
+ * ([n_heads, head_dim] bf16 each) of the sink (n_sink tokens, written once),
+ * of the current chunk (n_cur tokens, written every chunk) and of the
+ * history. Each layer's K and V live in one reserved virtual address range
+ * laid out as [sink | slot 0 | ... | slot S-1], one chunk per slot,
+ * S = hist_capacity / n_cur + 1: chunk c of an F-layer sits in slot c mod S
+ * and its history is every other filled slot, i.e. the min(c, S - 1) most
+ * recent chunks (a capacity at least as long as the stream keeps all of it).
+ * Physical memory is mapped, in pieces of at least 2 MiB, as slots are
+ * first used and released when a layer turns local-only, so resident memory
+ * follows the history that is actually kept. The chunk's K/V are written in place (into the pointers of
+ * ispa_kv_view_of, or with ispa_kv_write) and never move.
+ *
+ * Life cycle per chunk: write each layer's current K/V; run the layers
+ * (ispa_kv_attn / ispa_kv_layer_forward); then ispa_kv_advance once, which
+ * makes the chunk part of every F-layer's history. ispa_kv_evict_history
+ * turns a layer into an L-layer between chunks (after ispa_kv_advance and
+ * before the next chunk's K/V are written).
+ *
+ * The cache is host-side state: its calls are not thread-safe on one cache.
+ * ispa_kv_create, ispa_kv_advance, ispa_kv_evict_history and
+ * ispa_kv_destroy allocate or free device memory (HIP virtual memory
+ * management); the other calls only enqueue work like the calls above.
+ * ------------------------------------------------------------------------
+ */
+typedef struct ispa_kv_cache ispa_kv_cache;
+
+enum { ISPA_KV_CURRENT = 0, ISPA_KV_SINK = 1 };
+
+/* Where one layer's rows are, for the chunk that is current. */
+typedef struct ispa_kv_view {
+  void* k_sink; void* v_sink;   /* n_sink rows */
+  void* k_cur;  void* v_cur;    /* n_cur rows of the current chunk */
+  /* The three KV segments ispa_attn_decomp takes, in its order. When
+   * split_ok != 0 they are exactly (sink, current, history); otherwise (an
+   * F-layer whose ring has wrapped) their union is sink + history + current
+   * and only the full outputs are meaningful. A segment of length 0 has
+   * NULL pointers. */
+  const void* seg_k[3];
+  const void* seg_v[3];
+  int64_t seg_n[3];
+  int64_t n_hist;               /* history tokens */
+  int32_t split_ok;
+  int32_t local_only;           /* 1 after ispa_kv_evict_history */
+} ispa_kv_view;
+
+/*
+ * Create a cache on the current device. head_dim is 64 or 128;
+ * hist_capacity (tokens) must be a multiple of n_cur. Maps the sink and the
+ * first slot of every layer. *out is a host handle (NULL on error).
+ * Errors: ISPA_ERR_NULL (out), ISPA_ERR_SHAPE (n_layers, n_heads, n_cur < 1,
+ *   n_sink or hist_capacity < 0, hist_capacity % n_cur != 0, sizes that
+ *   overflow), ISPA_ERR_UNSUPPORTED (head_dim; device without virtual
+ *   memory management), ISPA_ERR_HIP (reservation or mapping failed, e.g.
+ *   out of device memory).
+ */
+int ispa_kv_create(int n_layers, int n_heads, int head_dim, int64_t n_sink,
+                   int64_t n_cur, int64_t hist_capacity, ispa_kv_cache** out);
+
+/* Waits for the device, then frees every range. ISPA_ERR_NULL for NULL. */
+int ispa_kv_destroy(ispa_kv_cache* cache);
+
+/* Host-side copy of layer `layer`'s view. Errors: ISPA_ERR_NULL,
+ * ISPA_ERR_SHAPE (layer out of range). */
+int ispa_kv_view_of(const ispa_kv_cache* cache, int layer, ispa_kv_view* view);
+
+/*
+ * Copy rows into the layer's current slot (which = ISPA_KV_CURRENT, n_cur
+ * rows) or sink (ISPA_KV_SINK, n_sink rows), device to device, on `stream`.
+ * k, v: [rows, n_heads, head_dim] bf16.
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (layer, which), ISPA_ERR_HIP.
+ */
+int ispa_kv_write(ispa_kv_cache* cache, int layer, int which, const void* k,
+                  const void* v, void* stream);
+
+/*
+ * End of a chunk: every F-layer's current chunk joins its history and the
+ * next slot is mapped (the oldest chunk is dropped once the ring is full).
+ * L-layers keep writing slot 0. Host call; enqueues nothing. On
+ * ISPA_ERR_HIP (mapping failed) no layer has moved.
+ */
+int ispa_kv_advance(ispa_kv_cache* cache);
+
+/*
+ * Turn a layer into an L-layer: waits for `stream` (work on other streams
+ * that reads the layer must be complete), then unmaps and frees its history;
+ * the sink and slot 0 stay. Idempotent. Errors: ISPA_ERR_NULL,
+ * ISPA_ERR_SHAPE, ISPA_ERR_HIP.
+ */
+int ispa_kv_evict_history(ispa_kv_cache* cache, int layer, void* stream);
+
+/* Text of the last failed HIP call made by the cache's management calls
+ * (which call, offset and size within the layer's range, HIP's message), or
+ * "" if none failed. With cache = NULL: the last failed ispa_kv_create on
+ * the calling thread. The text lives as long as the cache (or the thread). */
+const char* ispa_kv_last_error(const ispa_kv_cache* cache);
+
+/* Device bytes currently mapped for K and V of all layers (-1 for NULL). */
+int64_t ispa_kv_resident_bytes(const ispa_kv_cache* cache);
+
+/*
+ * ispa_attn_decomp of one layer over its cache for the current chunk:
+ * q [n_q, n_heads, head_dim] bf16, outputs as there. The split outputs
+ * (o_local, lse_local, o_hist, lse_hist, d_out) need split_ok (see
+ * ispa_kv_view); otherwise ISPA_ERR_UNSUPPORTED. For an L-layer the history
+ * is empty. Other errors as for ispa_attn_decomp, plus ISPA_ERR_SHAPE for
+ * the layer index.
+ */
+int ispa_kv_attn(const ispa_kv_cache* cache, int layer, const void* q,
+                 int64_t n_q, float sm_scale, void* o_local, float* lse_local,
+                 void* o_hist, float* lse_hist, void* o_full, float* lse_full,
+                 void* d_out, void* stream);
+
+/*
+ * One layer's attention and output projection in the stream: an L-layer
+ * computes O = local attention, an F-layer O = full attention (one pass),
+ * into o_tmp [n_q, h] bf16, then y = O wo^T ([n_q, h] bf16, h = n_heads *
+ * head_dim, wo [h, h] bf16 in nn.Linear layout: W + dW for an L-layer after
+ * ispa_apply_dW, W for an F-layer). Errors as ispa_kv_attn and ispa_project;
+ * nothing is enqueued on error.
+ */
+int ispa_kv_layer_forward(const ispa_kv_cache* cache, int layer, const void* q,
+                          int64_t n_q, float sm_scale, const void* wo,
+                          void* o_tmp, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ ISPA_ERR_HIP = 6
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m kv_cache_absorption_attn_amd.build`")
+        f"{LIB_PATH} is missing: build it with `python kv_cache_absorption_attn_amd/build.py`")
 try:
     lib = ct.CDLL(LIB_PATH)
 except OSError as exc:  # pragma: no cover - depends on the ROCm install
@@ -55,14 +55,51 @@ lib.ispa_apply_dW.argtypes = [_i, _i, _p, _p, _p, _p]
 lib.ispa_project.restype = _i
 lib.ispa_project.argtypes = [_p, _p, _p, _i64, _i, _i, _p]
 
+
+
+class KVView(ct.Structure):
+    """Mirror of ispa_kv_view (include/ispa.h)."""
+    _fields_ = [("k_sink", _p), ("v_sink", _p), ("k_cur", _p), ("v_cur", _p),
+                ("seg_k", _p * 3), ("seg_v", _p * 3), ("seg_n", _i64 * 3),
+                ("n_hist", _i64), ("split_ok", ct.c_int32), ("local_only", ct.c_int32)]
+
+
+lib.ispa_kv_create.restype = _i
+lib.ispa_kv_create.argtypes = [_i, _i, _i, _i64, _i64, _i64, ct.POINTER(_p)]
+lib.ispa_kv_destroy.restype = _i
+lib.ispa_kv_destroy.argtypes = [_p]
+lib.ispa_kv_view_of.restype = _i
+lib.ispa_kv_view_of.argtypes = [_p, _i, ct.POINTER(KVView)]
+lib.ispa_kv_write.restype = _i
+lib.ispa_kv_write.argtypes = [_p, _i, _i, _p, _p, _p]
+lib.ispa_kv_advance.restype = _i
+lib.ispa_kv_advance.argtypes = [_p]
+lib.ispa_kv_evict_history.restype = _i
+lib.ispa_kv_evict_history.argtypes = [_p, _i, _p]
+lib.ispa_kv_last_error.restype = ct.c_char_p
+lib.ispa_kv_last_error.argtypes = [_p]
+lib.ispa_kv_resident_bytes.restype = _i64
+lib.ispa_kv_resident_bytes.argtypes = [_p]
+lib.ispa_kv_attn.restype = _i
+lib.ispa_kv_attn.argtypes = [_p, _i, _p, _i64, _f, _p, _p, _p, _p, _p, _p, _p, _p]
+lib.ispa_kv_layer_forward.restype = _i
+lib.ispa_kv_layer_forward.argtypes = [_p, _i, _p, _i64, _f, _p, _p, _p, _p]
+
+ISPA_KV_CURRENT = 0
+ISPA_KV_SINK = 1
+
 EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram_accumulate",
             "ispa_ridge_workspace_bytes", "ispa_ridge_solve", "ispa_layer_score",
-            "ispa_apply_dW", "ispa_project")
+            "ispa_apply_dW", "ispa_project", "ispa_kv_create", "ispa_kv_destroy",
+            "ispa_kv_view_of", "ispa_kv_write", "ispa_kv_advance", "ispa_kv_evict_history",
+            "ispa_kv_last_error", "ispa_kv_resident_bytes", "ispa_kv_attn",
+            "ispa_kv_layer_forward")
 
 
 class IspaError(RuntimeError):
-    def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn}: {ispa_status_string(status)} (status {status})")
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        msg = f"{fn}: {ispa_status_string(status)} (status {status})"
+        super().__init__(msg + (f" [{detail}]" if detail else ""))
         self.status = status
 
 
@@ -191,3 +228,110 @@ def ispa_project(x, w, y, *, stream=None) -> None:
     st = lib.ispa_project(_ptr(x, torch.bfloat16, "x"), _ptr(w, torch.bfloat16, "w"),
                           _ptr(y, torch.bfloat16, "y"), n, h_in, h_out, _stream(stream))
     _check("ispa_project", st)
+
+
+class KVCache:
+    """Streaming KV cache of n_layers attention layers (ispa_kv_* in
+    include/ispa.h): sink, current chunk and history rows of every layer,
+    with the history's device memory mapped as it grows and released when a
+    layer turns local-only. The handle is freed by close() (or when the
+    object is collected)."""
+
+    def __init__(self, n_layers: int, n_heads: int, head_dim: int, n_sink: int, n_cur: int,
+                 hist_capacity: int):
+        h = _p()
+        self._h = _p()
+        st = lib.ispa_kv_create(n_layers, n_heads, head_dim, n_sink, n_cur, hist_capacity,
+                                ct.byref(h))
+        if st != ISPA_OK:
+            raise IspaError("ispa_kv_create", st, lib.ispa_kv_last_error(None).decode())
+        self._h = h
+        self.n_layers, self.n_heads, self.head_dim = n_layers, n_heads, head_dim
+        self.n_sink, self.n_cur, self.hist_capacity = n_sink, n_cur, hist_capacity
+
+    @property
+    def handle(self) -> int:
+        if not self._h:
+            raise ValueError("KVCache is closed")
+        return self._h.value
+
+    def _check(self, fn: str, status: int) -> None:
+        if status != ISPA_OK:
+            raise IspaError(fn, status, lib.ispa_kv_last_error(self._h).decode())
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            st = lib.ispa_kv_destroy(self._h)
+            self._h = _p()
+            _check("ispa_kv_destroy", st)
+
+    def __del__(self):  # pragma: no cover - depends on collection order
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def view(self, layer: int) -> KVView:
+        v = KVView()
+        _check("ispa_kv_view_of", lib.ispa_kv_view_of(self.handle, layer, ct.byref(v)))
+        return v
+
+    def _rows(self, t, n, name):
+        if tuple(t.shape) != (n, self.n_heads, self.head_dim):
+            raise ValueError(f"{name}: expected shape {(n, self.n_heads, self.head_dim)}")
+        return _ptr(t, torch.bfloat16, name)
+
+    def write(self, layer: int, k, v, *, sink: bool = False, stream=None) -> None:
+        """Copy k, v [rows, n_heads, head_dim] bf16 into the layer's current
+        slot (or its sink)."""
+        n = self.n_sink if sink else self.n_cur
+        st = lib.ispa_kv_write(self.handle, layer, ISPA_KV_SINK if sink else ISPA_KV_CURRENT,
+                               self._rows(k, n, "k"), self._rows(v, n, "v"), _stream(stream))
+        self._check("ispa_kv_write", st)
+
+    def advance(self) -> None:
+        self._check("ispa_kv_advance", lib.ispa_kv_advance(self.handle))
+
+    def evict_history(self, layer: int, *, stream=None) -> None:
+        self._check("ispa_kv_evict_history",
+                    lib.ispa_kv_evict_history(self.handle, layer, _stream(stream)))
+
+    def resident_bytes(self) -> int:
+        return int(lib.ispa_kv_resident_bytes(self.handle))
+
+    def attn(self, layer: int, q, sm_scale: float, *, o_local=None, lse_local=None, o_hist=None,
+             lse_hist=None, o_full=None, lse_full=None, d_out=None, stream=None) -> None:
+        bf, f32 = torch.bfloat16, torch.float32
+        n_q = q.shape[0]
+        h = self.n_heads * self.head_dim
+        if tuple(q.shape) != (n_q, self.n_heads, self.head_dim):
+            raise ValueError("q: shape mismatch")
+        for name, t in (("o_local", o_local), ("o_hist", o_hist), ("o_full", o_full),
+                        ("d_out", d_out)):
+            if t is not None and tuple(t.shape) != (n_q, h):
+                raise ValueError(f"{name}: expected shape {(n_q, h)}")
+        for name, t in (("lse_local", lse_local), ("lse_hist", lse_hist), ("lse_full", lse_full)):
+            if t is not None and tuple(t.shape) != (self.n_heads, n_q):
+                raise ValueError(f"{name}: expected shape {(self.n_heads, n_q)}")
+        st = lib.ispa_kv_attn(
+            self.handle, layer, _ptr(q, bf, "q"), n_q, float(sm_scale),
+            _ptr(o_local, bf, "o_local"), _ptr(lse_local, f32, "lse_local"),
+            _ptr(o_hist, bf, "o_hist"), _ptr(lse_hist, f32, "lse_hist"),
+            _ptr(o_full, bf, "o_full"), _ptr(lse_full, f32, "lse_full"),
+            _ptr(d_out, bf, "d_out"), _stream(stream))
+        _check("ispa_kv_attn", st)
+
+    def layer_forward(self, layer: int, q, sm_scale: float, wo, o_tmp, y, *, stream=None) -> None:
+        """y [n_q, h] = attention of the layer (local for an L-layer, full
+        otherwise) projected through wo [h, h]; o_tmp [n_q, h] receives O."""
+        bf = torch.bfloat16
+        n_q = q.shape[0]
+        h = self.n_heads * self.head_dim
+        if tuple(q.shape) != (n_q, self.n_heads, self.head_dim) or tuple(wo.shape) != (h, h) or \
+                tuple(o_tmp.shape) != (n_q, h) or tuple(y.shape) != (n_q, h):
+            raise ValueError("layer_forward: shape mismatch")
+        st = lib.ispa_kv_layer_forward(self.handle, layer, _ptr(q, bf, "q"), n_q,
+                                       float(sm_scale), _ptr(wo, bf, "wo"),
+                                       _ptr(o_tmp, bf, "o_tmp"), _ptr(y, bf, "y"),
+                                       _stream(stream))
+        _check("ispa_kv_layer_forward", st)

@@ -1,6 +1,9 @@
 """Build libispa.so (the ISPA C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m kv_cache_absorption_attn_amd.build [--jobs N]
+    python kv_cache_absorption_attn_amd/build.py [--jobs N]
+
+(run as a script: `python -m` would import the package, which loads the
+library this builds).
 
 Objects go to _build/ at the repository root; the shared library lands next
 to this file so the Python binding finds it.
@@ -21,7 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libispa.so")
 
-SOURCES = ["attn_decomp.hip", "gram.hip", "gemm_f32.hip", "solve.hip", "ispa_api.hip"]
+SOURCES = ["attn_decomp.hip", "gram.hip", "gemm_f32.hip", "solve.hip", "ispa_api.hip",
+           "kv_cache.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -173,7 +173,7 @@ const char* ispa_status_string(int status) {
     case ISPA_ERR_UNSUPPORTED: return "unsupported configuration";
     case ISPA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case ISPA_ERR_WORKSPACE: return "workspace missing or too small";
-    case ISPA_ERR_HIP: return "HIP runtime error at launch";
+    case ISPA_ERR_HIP: return "HIP runtime error (launch, copy or memory mapping)";
     default: return "unknown status";
   }
 }

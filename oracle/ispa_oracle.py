@@ -291,16 +291,32 @@ def project(x: np.ndarray, wo: np.ndarray) -> np.ndarray:
 # Whole warmup (ISPA paper §3.1 items 1-3) for small cases
 # ---------------------------------------------------------------------------
 
-def run_warmup_layer(steps, wo, lam: float, scale: float):
-    """steps: iterable of workloads.StepInputs for one layer.
-    Returns dict with stacked X/Z, statistics, dW and the error."""
+def stored_activations(o_local, o_full) -> Tuple[np.ndarray, np.ndarray]:
+    """The warmup activations as a bf16 model keeps them: X = bf16(O_local)
+    and D = bf16(O_full - O_local), each the rounding of its exact value, so
+    that D = 0 exactly when there is no history. (Reading: the pages do not
+    fix the precision of the collected activations; they are kept in the
+    model's bf16 activation dtype.)"""
+    o_local = np.asarray(o_local, dtype=np.float64)
+    return bf16_round(o_local), bf16_round(np.asarray(o_full, dtype=np.float64) - o_local)
+
+
+def run_warmup_layer(steps, wo, lam: float, scale: float, store_bf16: bool = False):
+    """steps: iterable of workloads.StepInputs for one layer. With
+    store_bf16 the statistics are taken over stored_activations (bf16 X and
+    D) instead of the exact fp64 ones. Returns dict with stacked X/Z,
+    statistics, dW and the error."""
     xs, ds, zs = [], [], []
     for st in steps:
         r = decomposable_attention(st.q, st.k_sink, st.v_sink, st.k_cur,
                                    st.v_cur, st.k_hist, st.v_hist, scale)
-        xs.append(r["o_local"])
-        ds.append(r["d"])
-        zs.append(r["o_full"])
+        if store_bf16:
+            x, d = stored_activations(r["o_local"], r["o_full"])
+        else:
+            x, d = r["o_local"], r["d"]
+        xs.append(x)
+        ds.append(d)
+        zs.append(x + d)
     g, c, e = gram_statistics(xs, ds)
     dw = ridge_delta_w(g, c, wo, lam)
     eps_abs, eps_rel = layer_error_from_stats(g, c, e, wo, dw, lam)

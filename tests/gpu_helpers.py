@@ -75,3 +75,27 @@ def compare_attention(gpu, ref, keys=None, o_tol=O_MAXABS, lse_tol=LSE_MAXABS, r
                 assert relf <= rel, f"{k}: rel fro {relf}"
             report[k] = (err, relf)
     return report
+
+
+def oracle_chain(w, layer=0, rows=None):
+    """The oracle's warmup of one layer with bf16-stored activations
+    (oracle.stored_activations), over every query row or over `rows` of each
+    step (attention rows are independent, so sampled rows are exact).
+    Returns the per-step X and D, the statistics, W_o, dW and the error."""
+    import workloads as wl
+    from oracle import ispa_oracle as orc
+    xs, ds = [], []
+    for s in range(w.n_steps):
+        st = wl.step_inputs(w, layer, s)
+        q = st.q if rows is None else st.q[rows]
+        r = orc.decomposable_attention(q, st.k_sink, st.v_sink, st.k_cur, st.v_cur, st.k_hist,
+                                       st.v_hist, w.sm_scale)
+        x, d = orc.stored_activations(r["o_local"], r["o_full"])
+        xs.append(x)
+        ds.append(d)
+    g, c, e = orc.gram_statistics(xs, ds)
+    wo = wl.output_projection(w, layer)
+    dw = orc.ridge_delta_w(g, c, wo, w.lam)
+    ea, er = orc.layer_error_from_stats(g, c, e, wo, dw, w.lam)
+    return {"xs": xs, "ds": ds, "g": g, "c": c, "e": e, "wo": wo, "dw": dw, "eps_abs": ea,
+            "eps_rel": er}

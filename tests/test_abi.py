@@ -114,3 +114,33 @@ def test_score_apply_project_validation():
     assert p(A, A, A, -4, 128, 128, 0) == SHAPE
     assert p(A, A, A, 4, 100, 128, 0) == UNSUP
     assert p(A, A, A, 0, 128, 128, 0) == OK
+
+
+def test_kv_cache_validation():
+    """Argument checks of the streaming KV cache that return before any HIP
+    call: bad shapes, NULL handles and NULL outputs."""
+    import ctypes as ct
+    L = _lib.lib
+    h = ct.c_void_p()
+    assert L.ispa_kv_create(2, 2, 128, 8, 16, 32, None) == NULL
+    assert L.ispa_kv_create(0, 2, 128, 8, 16, 32, ct.byref(h)) == SHAPE
+    assert L.ispa_kv_create(2, 0, 128, 8, 16, 32, ct.byref(h)) == SHAPE
+    assert L.ispa_kv_create(2, 2, 128, -1, 16, 32, ct.byref(h)) == SHAPE
+    assert L.ispa_kv_create(2, 2, 128, 8, 0, 32, ct.byref(h)) == SHAPE
+    assert L.ispa_kv_create(2, 2, 128, 8, 16, -16, ct.byref(h)) == SHAPE
+    assert L.ispa_kv_create(2, 2, 128, 8, 16, 40, ct.byref(h)) == SHAPE   # not whole chunks
+    assert L.ispa_kv_create(2, 2, 128, 8, 1 << 40, 1 << 60, ct.byref(h)) == SHAPE
+    assert L.ispa_kv_create(2, 2, 96, 8, 16, 32, ct.byref(h)) == UNSUP
+    assert h.value is None
+    view = _lib.KVView()
+    assert L.ispa_kv_destroy(None) == NULL
+    assert L.ispa_kv_view_of(None, 0, ct.byref(view)) == NULL
+    assert L.ispa_kv_write(None, 0, 0, A, A, 0) == NULL
+    assert L.ispa_kv_advance(None) == NULL
+    assert L.ispa_kv_evict_history(None, 0, 0) == NULL
+    assert L.ispa_kv_resident_bytes(None) == -1
+    L.ispa_kv_last_error.restype = ct.c_char_p
+    assert L.ispa_kv_last_error(None) == b""
+    assert L.ispa_kv_attn(None, 0, A, 4, 0.1, A, 0, 0, 0, 0, 0, 0, 0) == NULL
+    assert L.ispa_kv_layer_forward(None, 0, A, 4, 0.1, A, A, A, 0) == NULL
+    assert ct.sizeof(_lib.KVView) == 4 * 8 + 6 * 8 + 3 * 8 + 8 + 2 * 4

@@ -261,3 +261,40 @@ def test_project_brute():
     for i in range(3):
         for o in range(5):
             assert abs(y[i, o] - sum(x[i, j] * w[o, j] for j in range(4))) < 1e-13
+
+
+def test_stored_activations():
+    """X and D as a bf16 model keeps them: both are bf16 values within the
+    bf16 unit roundoff (2^-8) of O_local and of O_full - O_local, and D is 0
+    exactly without history (a D taken against the rounded X would keep the
+    rounding residual of X there)."""
+    rng = np.random.default_rng(21)
+    o_l = rng.standard_normal((50, 16))
+    o_f = o_l + 1e-3 * rng.standard_normal((50, 16))
+    x, d = orc.stored_activations(o_l, o_f)
+    np.testing.assert_array_equal(orc.bf16_round(x), x)
+    np.testing.assert_array_equal(orc.bf16_round(d), d)
+    assert np.all(np.abs(x - o_l) <= 2.0 ** -8 * np.abs(o_l))
+    assert np.all(np.abs(d - (o_f - o_l)) <= 2.0 ** -8 * np.abs(o_f - o_l))
+    x0, d0 = orc.stored_activations(o_l, o_l)
+    np.testing.assert_array_equal(x0, x)
+    assert np.count_nonzero(d0) == 0
+
+
+def test_warmup_with_stored_activations():
+    w = wl.TINY
+    steps = [wl.step_inputs(w, 0, s) for s in range(w.n_steps)]
+    wo = wl.output_projection(w, 0)
+    r = orc.run_warmup_layer(steps, wo, w.lam, w.sm_scale, store_bf16=True)
+    np.testing.assert_array_equal(orc.bf16_round(r["x_all"]), r["x_all"])
+    np.testing.assert_array_equal(orc.bf16_round(r["d_all"]), r["d_all"])
+    g, c, e = orc.gram_statistics([r["x_all"]], [r["d_all"]])
+    np.testing.assert_allclose(r["g"], g, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["c"], c, rtol=1e-12, atol=1e-12)
+    exact = orc.run_warmup_layer(steps, wo, w.lam, w.sm_scale)
+    # bf16 storage moves the statistics by a few 1e-4 relative on this case,
+    # and dW by under 1e-3 (the GPU chain test's tolerance is derived from it)
+    rel = np.linalg.norm(r["g"] - exact["g"]) / np.linalg.norm(exact["g"])
+    assert 0 < rel < 2e-3
+    rel_dw = np.linalg.norm(r["dw"] - exact["dw"]) / np.linalg.norm(exact["dw"])
+    assert 0 < rel_dw < 2e-3
