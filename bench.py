@@ -189,71 +189,81 @@ def summarize_events(timing):
 
 
 def stream_measure(ispa, w: wl.Workload, frames=(60, 120), reps: int = 2, seed: int = 1):
-    """Long-horizon streaming after absorption (14B-class): per-chunk time of
-    the attention + output projection of all layers, for the ISPA split
-    (k_select L-layers on local KV, the rest full) against every layer full,
-    at history lengths of `frames` latent frames. The history KV of every
-    layer is resident (the all-full run needs it); the KV bytes reported for
-    ISPA count what its layers keep."""
+    """Long-horizon streaming after absorption (14B-class) through the KV
+    cache (ispa_kv_*): chunks of 3 latent frames stream in and every
+    full-history layer's history grows, chunk by chunk, to `frames` latent
+    frames. Two runs, one after the other: ISPA (k_select L-layers, every
+    other layer, whose history is evicted at the transition; the rest
+    F-layers) and every layer full. At each listed history length the
+    attention + output projection of all layers for one chunk is timed with
+    HIP events (`reps` passes); writing the chunk K/V into the cache (a copy
+    here, the K/V projection's own output in a model) is not timed, and the
+    host time of advancing the cache (mapping the next slot's pages) is
+    reported beside it. KV bytes are the cache's mapped bytes."""
     dev, bf = "cuda", torch.bfloat16
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
     nh, d, h = w.n_heads, w.head_dim, w.hidden
     tok_per_frame = w.n_cur // 3
-    hmax = tok_per_frame * max(frames)
+    chunk_frames = w.n_cur // tok_per_frame
+    targets = {fr // chunk_frames: fr for fr in frames}
+    n_chunks = max(targets) + 1
 
     def rnd(*shape):
         return (torch.randn(*shape, generator=g, device=dev) * w.qkv_std).to(bf)
 
     L = w.n_layers
     q = [rnd(w.n_q, nh, d) for _ in range(L)]
-    ks = [rnd(w.n_sink, nh, d) for _ in range(L)]
-    vs = [rnd(w.n_sink, nh, d) for _ in range(L)]
-    kc = [rnd(w.n_cur, nh, d) for _ in range(L)]
-    vc = [rnd(w.n_cur, nh, d) for _ in range(L)]
-    kh = [rnd(hmax, nh, d) for _ in range(L)]
-    vh = [rnd(hmax, nh, d) for _ in range(L)]
+    k_sink, v_sink = rnd(w.n_sink, nh, d), rnd(w.n_sink, nh, d)
+    k_chunk, v_chunk = rnd(w.n_cur, nh, d), rnd(w.n_cur, nh, d)
     wo = rnd(L, h, h)
     x = torch.empty(w.n_q, h, dtype=bf, device=dev)
     y = torch.empty_like(x)
-    is_l = [l % 2 == 0 for l in range(L)]  # every other layer is an L-layer
+    is_l = [l % 2 == 0 for l in range(L)]
     assert sum(is_l) == w.k_select
-    kv_tok_bytes = nh * d * 2 * 2
 
-    def chunk(n_hist, ispa_split):
+    def one_chunk(cache):
         for l in range(L):
-            if ispa_split and is_l[l]:
-                ispa.ispa_attn_decomp(q[l], ks[l], vs[l], kc[l], vc[l], None, None, w.sm_scale,
-                                      o_local=x)
-            else:
-                ispa.ispa_attn_decomp(q[l], ks[l], vs[l], kc[l], vc[l], kh[l][:n_hist],
-                                      vh[l][:n_hist], w.sm_scale, o_full=x)
-            ispa.ispa_project(x, wo[l], y)
+            cache.layer_forward(l, q[l], w.sm_scale, wo[l], x, y)
 
     res = {"frames": list(frames), "l_layers": sum(is_l), "f_layers": L - sum(is_l),
-           "ispa_ms": [], "all_full_ms": [], "speedup": [], "ispa_kv_gb": [], "all_full_kv_gb": []}
-    for fr in frames:
-        n_hist = tok_per_frame * fr
-        times = {}
-        for split in (True, False):
-            chunk(n_hist, split)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                chunk(n_hist, split)
-            e1.record()
-            torch.cuda.synchronize()
-            times[split] = e0.elapsed_time(e1) / reps
-        local = w.n_sink + w.n_cur
-        res["ispa_ms"].append(round(times[True], 2))
-        res["all_full_ms"].append(round(times[False], 2))
-        res["speedup"].append(round(times[False] / times[True], 3))
-        res["ispa_kv_gb"].append(round(kv_tok_bytes * (sum(is_l) * local + (L - sum(is_l)) *
-                                                       (local + n_hist)) / 1e9, 2))
-        res["all_full_kv_gb"].append(round(kv_tok_bytes * L * (local + n_hist) / 1e9, 2))
-        print(f"[bench] stream {fr} frames: ispa {times[True]:.1f} ms, all-full "
-              f"{times[False]:.1f} ms", file=sys.stderr, flush=True)
+           "ispa_ms": [], "all_full_ms": [], "speedup": [], "ispa_kv_gb": [],
+           "all_full_kv_gb": [], "ispa_advance_host_ms": None, "all_full_advance_host_ms": None}
+    for split in (True, False):
+        tag = "ispa" if split else "all_full"
+        cache = ispa.KVCache(L, nh, d, w.n_sink, w.n_cur, (n_chunks - 1) * w.n_cur)
+        try:
+            for l in range(L):
+                cache.write(l, k_sink, v_sink, sink=True)
+                if split and is_l[l]:
+                    cache.evict_history(l)
+            adv_s = 0.0
+            for c in range(n_chunks):
+                for l in range(L):
+                    cache.write(l, k_chunk, v_chunk)
+                if c in targets:
+                    one_chunk(cache)
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(reps):
+                        one_chunk(cache)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ms = e0.elapsed_time(e1) / reps
+                    res[f"{tag}_ms"].append(round(ms, 2))
+                    res[f"{tag}_kv_gb"].append(round(cache.resident_bytes() / 1e9, 2))
+                    print(f"[bench] stream {tag} {targets[c]} frames: {ms:.1f} ms per chunk, "
+                          f"{cache.resident_bytes() / 1e9:.1f} GB KV", file=sys.stderr, flush=True)
+                if c + 1 < n_chunks:
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    cache.advance()
+                    adv_s += time.perf_counter() - t0
+            res[f"{tag}_advance_host_ms"] = round(adv_s / max(1, n_chunks - 1) * 1e3, 3)
+        finally:
+            cache.close()
+    res["speedup"] = [round(f / i, 3) for i, f in zip(res["ispa_ms"], res["all_full_ms"])]
     return res
 
 

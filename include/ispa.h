@@ -196,9 +196,10 @@ int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in,
  * S = hist_capacity / n_cur + 1: chunk c of an F-layer sits in slot c mod S
  * and its history is every other filled slot, i.e. the min(c, S - 1) most
  * recent chunks (a capacity at least as long as the stream keeps all of it).
- * Physical memory is mapped, in pieces of at least 2 MiB, as slots are
- * first used and released when a layer turns local-only, so resident memory
- * follows the history that is actually kept. The chunk's K/V are written in place (into the pointers of
+ * Physical memory is mapped page by page as slots are first used (a page
+ * is the smallest power of two holding one chunk, 2 MiB to 256 MiB) and
+ * released when a layer turns local-only, so resident memory follows the
+ * history that is actually kept, to within one page per layer and tensor. The chunk's K/V are written in place (into the pointers of
  * ispa_kv_view_of, or with ispa_kv_write) and never move.
  *
  * Life cycle per chunk: write each layer's current K/V; run the layers

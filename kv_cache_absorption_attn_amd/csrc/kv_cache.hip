@@ -54,11 +54,21 @@ struct LayerKV {
 
 size_t round_up(size_t v, size_t g) { return (v + g - 1) / g * g; }
 
-// Memory is mapped in pages of one fixed size, at least 2 MiB (the large-page
-// size), each its own allocation, mapping and access grant: every mapping
-// call sees the same size and alignment whatever the chunk size, and a
-// layer's history is released page by page.
-constexpr size_t kPieceMin = size_t{2} << 20;
+// Memory is mapped in pages of one size per cache, each its own allocation,
+// mapping and access grant, naturally aligned in the range: the smallest
+// power of two that holds one chunk's rows, at least 2 MiB (the large-page
+// size) and at most 256 MiB. A full-history layer then maps about one page
+// per chunk, which keeps the number of live mappings (each a process
+// mapping of its own) in the thousands for 14B-sized histories, where 2 MiB
+// pages would need tens of thousands; the waste is under one page per range.
+constexpr size_t kPageMin = size_t{2} << 20;
+constexpr size_t kPageMax = size_t{256} << 20;
+
+size_t page_size(size_t chunk_bytes, size_t gran) {
+  size_t p = kPageMin;
+  while (p < chunk_bytes && p < kPageMax) p <<= 1;
+  return round_up(p > gran ? p : gran, gran);
+}
 
 // Text of the last failed HIP call (per cache; per thread for creation).
 struct ErrText {
@@ -242,7 +252,7 @@ int ispa_kv_create(int n_layers, int n_heads, int head_dim, int64_t n_sink, int6
     g_create_error.set("hipMemGetAllocationGranularity", ge, 0, gran);
     return ISPA_ERR_HIP;
   }
-  const size_t piece = round_up(kPieceMin > gran ? kPieceMin : gran, gran);
+  const size_t piece = page_size(static_cast<size_t>(n_cur) * row, gran);
 
   ispa_kv_cache* c = new (std::nothrow) ispa_kv_cache();
   if (!c) return ISPA_ERR_HIP;
