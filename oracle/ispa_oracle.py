@@ -355,3 +355,33 @@ def stream_layer_chunk(q, k_sink, v_sink, k_chunks, v_chunks, c: int, wo,
     v = np.concatenate([v_sink] + [v_chunks[i] for i in hist] + [v_chunks[c]], axis=0)
     o, _ = multihead_attention(q, k, v, scale)
     return o, project(o, wo)
+
+
+# ---------------------------------------------------------------------------
+# Event-triggered recalibration (ISPA paper §3.3, last paragraph: on a large
+# scene transition or temporal distribution shift the warmup-to-absorption
+# procedure is re-entered: dual-stream warmup again, errors recomputed, the
+# absorbed layer set and dW refreshed for the new context). The pages give no
+# trigger; the reading used here is a drift score of an L-layer's local
+# outputs against the warmup statistics its dW was fitted on.
+# ---------------------------------------------------------------------------
+
+def drift_reference(g: np.ndarray, lam: float, n_warm: int) -> float:
+    """Expected leverage x (G + lam I)^{-1} x^T of a warmup token:
+    tr((G + lam I)^{-1} G) / N, N the number of warmup tokens in G."""
+    g = np.asarray(g, dtype=np.float64)
+    m = g + lam * np.eye(g.shape[0])
+    return float(np.trace(np.linalg.solve(m, g)) / n_warm)
+
+
+def drift_score(x: np.ndarray, g: np.ndarray, lam: float, n_warm: int) -> float:
+    """Mean leverage of the rows of x (a sample of a chunk's local outputs
+    X = O_local of one layer) under the warmup statistics, divided by its
+    warmup expectation: 1 on average for tokens like the warmup ones, large
+    when the chunk's activations leave the span the ridge fit was supported
+    on (there the absorbed dW extrapolates)."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = g + lam * np.eye(g.shape[0])
+    lev = np.einsum("ij,ji->i", x, np.linalg.solve(m, x.T))
+    return float(lev.mean() / drift_reference(g, lam, n_warm))
