@@ -181,6 +181,40 @@ int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in,
                  int h_out, void* stream);
 
 /*
+ * Drift score for event-triggered recalibration (§3.3, last paragraph: on a
+ * large scene transition or temporal distribution shift the warmup-to-
+ * absorption procedure is re-entered; the pages give no trigger). For an
+ * absorbed layer with warmup statistics G over N warmup tokens and
+ * M = G + lambda I, the leverage of a token x (a row of the layer's local
+ * output X) is x M^{-1} x^T, and its warmup expectation is
+ * ref = tr(M^{-1} G) / N = (h - lambda tr(M^{-1})) / N. The score of a chunk
+ * is the mean leverage of a strided sample of its tokens divided by ref:
+ * about 1 while the activations stay in the span the update was fitted on,
+ * large once they leave it (the absorbed dW then extrapolates).
+ *
+ * ispa_drift_prepare: for each layer, the lower Cholesky factor of M is
+ *   inverted into linv ([n_layers][h, h] fp32, lower triangular, zeros
+ *   above the diagonal) and ref [n_layers] fp64 is computed. info as for
+ *   ispa_ridge_solve (linv and ref are meaningless where info != 0).
+ *   workspace: ispa_ridge_workspace_bytes(n_layers, h) bytes at least.
+ * ispa_drift_score: x [n_layers][n_tok, h] bf16; the sample is the rows
+ *   0, stride, 2 stride, ... (ceil(n_tok / stride) of them); score
+ *   [n_layers] fp64 out (+inf when ref is 0). workspace:
+ *   ispa_drift_workspace_bytes(n_layers, h, ceil(n_tok / stride)) bytes.
+ * ispa_drift_workspace_bytes covers both calls (0 for invalid sizes).
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (sizes < 1, lambda < 0 or not
+ *   finite), ISPA_ERR_UNSUPPORTED (h % 8 != 0), ISPA_ERR_WORKSPACE,
+ *   ISPA_ERR_ALIGN.
+ */
+size_t ispa_drift_workspace_bytes(int n_layers, int h, int64_t n_sample);
+int ispa_drift_prepare(int n_layers, int h, const float* G, float lambda,
+                       int64_t n_warm, float* linv, double* ref, int* info,
+                       void* workspace, size_t ws_bytes, void* stream);
+int ispa_drift_score(int n_layers, int h, const float* linv, const double* ref,
+                     const void* x, int64_t n_tok, int64_t stride, double* score,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * ------------------------------------------------------------------------
  * Streaming KV cache and the per-layer streaming step (§3.1 item 3 and
  * §3.3: after the transition the K selected layers (L-layers) attend the
@@ -286,6 +320,15 @@ int ispa_kv_evict_history(ispa_kv_cache* cache, int layer, void* stream);
  * the calling thread. The text lives as long as the cache (or the thread). */
 const char* ispa_kv_last_error(const ispa_kv_cache* cache);
 
+/*
+ * Turn an L-layer back into a full-history layer for a recalibration
+ * (§3.3, last paragraph): its history restarts empty with the current chunk
+ * (slot 0), and grows again from the next ispa_kv_advance. Call between
+ * chunks, like ispa_kv_evict_history. No effect on a full-history layer.
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE.
+ */
+int ispa_kv_restore_history(ispa_kv_cache* cache, int layer);
+
 /* Device bytes currently mapped for K and V of all layers (-1 for NULL). */
 int64_t ispa_kv_resident_bytes(const ispa_kv_cache* cache);
 
@@ -313,6 +356,89 @@ int ispa_kv_attn(const ispa_kv_cache* cache, int layer, const void* q,
 int ispa_kv_layer_forward(const ispa_kv_cache* cache, int layer, const void* q,
                           int64_t n_q, float sm_scale, const void* wo,
                           void* o_tmp, void* y, void* stream);
+
+/*
+ * ------------------------------------------------------------------------
+ * Streaming session: the warmup -> absorption -> streaming life cycle of all
+ * attention layers over one KV cache (§3.1 items 1-3, §3.3), with
+ * event-triggered recalibration (§3.3, last paragraph) driven by the drift
+ * score above. Host-side control; every step is one of the calls above,
+ * enqueued on the caller's stream.
+ *
+ * Per chunk: write every layer's current K/V (ispa_session_cache +
+ * ispa_kv_view_of / ispa_kv_write; the sink once, before the first chunk),
+ * run ispa_session_layer for each layer in order, then
+ * ispa_session_end_chunk once. The queries of a chunk are its n_cur tokens.
+ *  - warmup phase (from creation, and after a recalibration): every layer
+ *    runs the dual-stream attention, accumulates G, C, E over the phase's
+ *    chunks (statistics start over with each warmup) and outputs
+ *    y = O_full W^T with the original W. After t_warm chunks, end_chunk
+ *    solves dW against the original W, scores, selects k_select layers,
+ *    writes bf16(W + dW) for them into w_active, drops their history and
+ *    (drift_threshold > 0) prepares their drift state: event ABSORBED.
+ *  - stream phase: L-layers y = O_local (W + dW)^T, F-layers
+ *    y = O_full W^T; each L-layer's O_local gets a drift score (sample
+ *    stride drift_stride). If one exceeds drift_threshold (or is NaN),
+ *    end_chunk restores the L-layers (original W, history restarting with
+ *    the next chunk) and enters warmup again: event RECALIBRATE.
+ * The split attention of a warmup needs every F-layer's history in one
+ * piece, i.e. a ring that has not wrapped (ISPA_ERR_UNSUPPORTED otherwise):
+ * give hist_capacity at least the stream's length when recalibration is on.
+ *
+ * Memory: wo [n_layers][h, h] bf16 (original weights, read, kept unchanged
+ * by the caller), w_active [n_layers][h, h] bf16 (written: the weights in
+ * use), workspace of ispa_session_workspace_bytes bytes (statistics, dW,
+ * drift factors, solver scratch, one chunk of activations); the session's
+ * KV cache allocates its own pages. end_chunk synchronises `stream` at the
+ * transition and, with recalibration on, at every streaming chunk (it reads
+ * the selection and the drift scores on the host).
+ * ------------------------------------------------------------------------
+ */
+typedef struct ispa_session ispa_session;
+
+enum { ISPA_PHASE_WARMUP = 0, ISPA_PHASE_STREAM = 1 };
+enum { ISPA_EVENT_NONE = 0, ISPA_EVENT_ABSORBED = 1, ISPA_EVENT_RECALIBRATE = 2 };
+
+typedef struct ispa_session_config {
+  int32_t n_layers, n_heads, head_dim;   /* head_dim 64 or 128 */
+  int32_t k_select;                      /* layers absorbed per transition */
+  int32_t t_warm;                        /* warmup chunks per calibration (>= 1) */
+  int32_t reserved;
+  int64_t n_sink, n_cur, hist_capacity;  /* tokens; hist_capacity % n_cur == 0 */
+  float sm_scale, lambda;
+  double drift_threshold;                /* <= 0: never recalibrate */
+  int64_t drift_stride;                  /* >= 1 */
+} ispa_session_config;
+
+typedef struct ispa_session_state {
+  int32_t phase, warm_count, n_calibrations, reserved;
+  int64_t chunk;                         /* chunks ended so far */
+} ispa_session_state;
+
+/* Workspace bytes for a configuration (0 if it is invalid). */
+size_t ispa_session_workspace_bytes(const ispa_session_config* cfg);
+
+/* Create a session (and its KV cache) on the current device; copies wo into
+ * w_active on `stream`. Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (invalid
+ * configuration), ISPA_ERR_UNSUPPORTED, ISPA_ERR_WORKSPACE, ISPA_ERR_ALIGN,
+ * and those of ispa_kv_create. */
+int ispa_session_create(const ispa_session_config* cfg, const void* wo,
+                        void* w_active, void* workspace, size_t ws_bytes,
+                        void* stream, ispa_session** out);
+int ispa_session_destroy(ispa_session* s);
+/* The session's KV cache, to write the chunks' K/V (NULL for NULL). */
+ispa_kv_cache* ispa_session_cache(ispa_session* s);
+/* One layer of the current chunk: q [n_cur, n_heads, head_dim] bf16,
+ * y [n_cur, h] bf16 out. Errors of the calls it makes. */
+int ispa_session_layer(ispa_session* s, int layer, const void* q, void* y,
+                       void* stream);
+/* End of a chunk; *event (may be NULL) receives ISPA_EVENT_*. */
+int ispa_session_end_chunk(ispa_session* s, void* stream, int* event);
+/* Phase and counters; with non-NULL host arrays of n_layers entries also
+ * the current L-layer mask, the errors of the last transition and the last
+ * drift scores (0 for F-layers). */
+int ispa_session_query(const ispa_session* s, ispa_session_state* out,
+                       int* is_local, double* eps_rel, double* drift);
 
 #ifdef __cplusplus
 }

@@ -76,6 +76,50 @@ lib.ispa_kv_advance.restype = _i
 lib.ispa_kv_advance.argtypes = [_p]
 lib.ispa_kv_evict_history.restype = _i
 lib.ispa_kv_evict_history.argtypes = [_p, _i, _p]
+lib.ispa_kv_restore_history.restype = _i
+lib.ispa_kv_restore_history.argtypes = [_p, _i]
+lib.ispa_drift_workspace_bytes.restype = _sz
+lib.ispa_drift_workspace_bytes.argtypes = [_i, _i, _i64]
+lib.ispa_drift_prepare.restype = _i
+lib.ispa_drift_prepare.argtypes = [_i, _i, _p, _f, _i64, _p, _p, _p, _p, _sz, _p]
+lib.ispa_drift_score.restype = _i
+lib.ispa_drift_score.argtypes = [_i, _i, _p, _p, _p, _i64, _i64, _p, _p, _sz, _p]
+
+
+class SessionConfig(ct.Structure):
+    """Mirror of ispa_session_config (include/ispa.h)."""
+    _fields_ = [("n_layers", ct.c_int32), ("n_heads", ct.c_int32), ("head_dim", ct.c_int32),
+                ("k_select", ct.c_int32), ("t_warm", ct.c_int32), ("reserved", ct.c_int32),
+                ("n_sink", _i64), ("n_cur", _i64), ("hist_capacity", _i64),
+                ("sm_scale", ct.c_float), ("lam", ct.c_float), ("drift_threshold", ct.c_double),
+                ("drift_stride", _i64)]
+
+
+class SessionState(ct.Structure):
+    """Mirror of ispa_session_state (include/ispa.h)."""
+    _fields_ = [("phase", ct.c_int32), ("warm_count", ct.c_int32),
+                ("n_calibrations", ct.c_int32), ("reserved", ct.c_int32), ("chunk", _i64)]
+
+
+lib.ispa_session_workspace_bytes.restype = _sz
+lib.ispa_session_workspace_bytes.argtypes = [ct.POINTER(SessionConfig)]
+lib.ispa_session_create.restype = _i
+lib.ispa_session_create.argtypes = [ct.POINTER(SessionConfig), _p, _p, _p, _sz, _p,
+                                    ct.POINTER(_p)]
+lib.ispa_session_destroy.restype = _i
+lib.ispa_session_destroy.argtypes = [_p]
+lib.ispa_session_cache.restype = _p
+lib.ispa_session_cache.argtypes = [_p]
+lib.ispa_session_layer.restype = _i
+lib.ispa_session_layer.argtypes = [_p, _i, _p, _p, _p]
+lib.ispa_session_end_chunk.restype = _i
+lib.ispa_session_end_chunk.argtypes = [_p, _p, ct.POINTER(_i)]
+lib.ispa_session_query.restype = _i
+lib.ispa_session_query.argtypes = [_p, ct.POINTER(SessionState), _p, _p, _p]
+
+ISPA_PHASE_WARMUP, ISPA_PHASE_STREAM = 0, 1
+ISPA_EVENT_NONE, ISPA_EVENT_ABSORBED, ISPA_EVENT_RECALIBRATE = 0, 1, 2
+
 lib.ispa_kv_last_error.restype = ct.c_char_p
 lib.ispa_kv_last_error.argtypes = [_p]
 lib.ispa_kv_resident_bytes.restype = _i64
@@ -93,7 +137,10 @@ EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram
             "ispa_apply_dW", "ispa_project", "ispa_kv_create", "ispa_kv_destroy",
             "ispa_kv_view_of", "ispa_kv_write", "ispa_kv_advance", "ispa_kv_evict_history",
             "ispa_kv_last_error", "ispa_kv_resident_bytes", "ispa_kv_attn",
-            "ispa_kv_layer_forward")
+            "ispa_kv_layer_forward", "ispa_kv_restore_history", "ispa_drift_workspace_bytes",
+            "ispa_drift_prepare", "ispa_drift_score", "ispa_session_workspace_bytes",
+            "ispa_session_create", "ispa_session_destroy", "ispa_session_cache",
+            "ispa_session_layer", "ispa_session_end_chunk", "ispa_session_query")
 
 
 class IspaError(RuntimeError):
@@ -296,6 +343,9 @@ class KVCache:
         self._check("ispa_kv_evict_history",
                     lib.ispa_kv_evict_history(self.handle, layer, _stream(stream)))
 
+    def restore_history(self, layer: int) -> None:
+        self._check("ispa_kv_restore_history", lib.ispa_kv_restore_history(self.handle, layer))
+
     def resident_bytes(self) -> int:
         return int(lib.ispa_kv_resident_bytes(self.handle))
 
@@ -335,3 +385,117 @@ class KVCache:
                                        _ptr(o_tmp, bf, "o_tmp"), _ptr(y, bf, "y"),
                                        _stream(stream))
         _check("ispa_kv_layer_forward", st)
+
+
+def ispa_drift_workspace_bytes(n_layers: int, h: int, n_sample: int) -> int:
+    return int(lib.ispa_drift_workspace_bytes(n_layers, h, n_sample))
+
+
+def ispa_drift_prepare(G, lam: float, n_warm: int, linv, ref, info, workspace, *,
+                       stream=None) -> None:
+    """G [L, h, h] fp32 -> linv [L, h, h] fp32, ref [L] fp64, info [L] int32."""
+    n_layers, h, _ = G.shape
+    st = lib.ispa_drift_prepare(n_layers, h, _ptr(G, torch.float32, "G"), float(lam), int(n_warm),
+                                _ptr(linv, torch.float32, "linv"),
+                                _ptr(ref, torch.float64, "ref"), _ptr(info, torch.int32, "info"),
+                                _ptr(workspace, None, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ispa_drift_prepare", st)
+
+
+def ispa_drift_score(linv, ref, x, stride: int, score, workspace, *, stream=None) -> None:
+    """x [L, n_tok, h] (or [n_tok, h]) bf16 -> score [L] fp64."""
+    if x.dim() == 2:
+        x = x.unsqueeze(0)
+    n_layers, n_tok, h = x.shape
+    if tuple(linv.shape) != (n_layers, h, h) or ref.shape[0] != n_layers or \
+            score.shape[0] != n_layers:
+        raise ValueError("ispa_drift_score: shape mismatch")
+    st = lib.ispa_drift_score(n_layers, h, _ptr(linv, torch.float32, "linv"),
+                              _ptr(ref, torch.float64, "ref"), _ptr(x, torch.bfloat16, "x"),
+                              n_tok, int(stride), _ptr(score, torch.float64, "score"),
+                              _ptr(workspace, None, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ispa_drift_score", st)
+
+
+class Session:
+    """ISPA streaming session (ispa_session_* in include/ispa.h): warmup,
+    absorption and streaming of all layers over one KV cache, with
+    event-triggered recalibration. wo [L, h, h] bf16 holds the original
+    weights (kept unchanged); the session owns the active weights and its
+    workspace as torch tensors."""
+
+    def __init__(self, wo, *, n_heads: int, head_dim: int, n_sink: int, n_cur: int,
+                 hist_capacity: int, k_select: int, t_warm: int, sm_scale: float, lam: float,
+                 drift_threshold: float = 0.0, drift_stride: int = 1, stream=None):
+        n_layers = wo.shape[0]
+        self.cfg = SessionConfig(n_layers, n_heads, head_dim, k_select, t_warm, 0, n_sink, n_cur,
+                                 hist_capacity, sm_scale, lam, drift_threshold, drift_stride)
+        nbytes = int(lib.ispa_session_workspace_bytes(ct.byref(self.cfg)))
+        if nbytes == 0:
+            raise IspaError("ispa_session_workspace_bytes", ISPA_ERR_SHAPE)
+        self.wo = wo
+        self.w_active = torch.empty_like(wo)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=wo.device)
+        self.n_layers, self.n_cur = n_layers, n_cur
+        self.h = n_heads * head_dim
+        h = _p()
+        self._h = _p()
+        st = lib.ispa_session_create(ct.byref(self.cfg), _ptr(wo, torch.bfloat16, "wo"),
+                                     _ptr(self.w_active, torch.bfloat16, "w_active"),
+                                     _ptr(self.workspace, None, "workspace"), nbytes,
+                                     _stream(stream), ct.byref(h))
+        if st != ISPA_OK:
+            raise IspaError("ispa_session_create", st, lib.ispa_kv_last_error(None).decode())
+        self._h = h
+        cache = KVCache.__new__(KVCache)
+        cache._h = _p(lib.ispa_session_cache(h))
+        cache.n_layers, cache.n_heads, cache.head_dim = n_layers, n_heads, head_dim
+        cache.n_sink, cache.n_cur, cache.hist_capacity = n_sink, n_cur, hist_capacity
+        cache.close = lambda: None          # owned by the session
+        self.cache = cache
+
+    @property
+    def handle(self) -> int:
+        if not self._h:
+            raise ValueError("Session is closed")
+        return self._h.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            st = lib.ispa_session_destroy(self._h)
+            self._h = _p()
+            self.cache._h = _p()
+            _check("ispa_session_destroy", st)
+
+    def __del__(self):  # pragma: no cover - depends on collection order
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def layer(self, layer: int, q, y, *, stream=None) -> None:
+        if tuple(y.shape) != (self.n_cur, self.h) or q.shape[0] != self.n_cur:
+            raise ValueError("Session.layer: shape mismatch")
+        st = lib.ispa_session_layer(self.handle, layer, _ptr(q, torch.bfloat16, "q"),
+                                    _ptr(y, torch.bfloat16, "y"), _stream(stream))
+        if st != ISPA_OK:
+            raise IspaError("ispa_session_layer", st, lib.ispa_kv_last_error(self.cache._h).decode())
+
+    def end_chunk(self, *, stream=None) -> int:
+        ev = _i(0)
+        st = lib.ispa_session_end_chunk(self.handle, _stream(stream), ct.byref(ev))
+        if st != ISPA_OK:
+            raise IspaError("ispa_session_end_chunk", st,
+                            lib.ispa_kv_last_error(self.cache._h).decode())
+        return int(ev.value)
+
+    def state(self):
+        """(SessionState, is_local list, eps_rel list, drift list)."""
+        st = SessionState()
+        L = self.n_layers
+        loc, eps, dr = (ct.c_int * L)(), (ct.c_double * L)(), (ct.c_double * L)()
+        _check("ispa_session_query", lib.ispa_session_query(
+            self.handle, ct.byref(st), ct.cast(loc, _p), ct.cast(eps, _p), ct.cast(dr, _p)))
+        return st, list(loc), list(eps), list(dr)

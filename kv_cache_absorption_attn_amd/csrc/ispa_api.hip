@@ -363,6 +363,69 @@ int ispa_apply_dW(int n_layers, int h, const int* selected, const float* dW, voi
                                           static_cast<uint16_t*>(Wo), as_stream(stream)));
 }
 
+size_t ispa_drift_workspace_bytes(int n_layers, int h, int64_t n_sample) {
+  if (n_layers < 1 || h < 1 || n_sample < 1) return 0;
+  const size_t ridge = ridge_layout(nullptr, n_layers, h).bytes;
+  const size_t y = align_up(static_cast<size_t>(n_layers) * h * n_sample * sizeof(float)) +
+                   align_up(static_cast<size_t>(n_layers) * ispa::drift_partial_count(h) *
+                            sizeof(double));
+  return ridge > y ? ridge : y;
+}
+
+int ispa_drift_prepare(int n_layers, int h, const float* G, float lambda, int64_t n_warm,
+                       float* linv, double* ref, int* info, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  if (!G || !linv || !ref || !info) return ISPA_ERR_NULL;
+  if (n_layers < 1 || h < 1 || n_warm < 1 || !(lambda >= 0.f) || !isfinite(lambda))
+    return ISPA_ERR_SHAPE;
+  if (h % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < ridge_layout(nullptr, n_layers, h).bytes) return ISPA_ERR_WORKSPACE;
+  if (!aligned16(G) || !aligned16(linv) || !aligned16(ref) || !aligned16(info) ||
+      !aligned16(workspace))
+    return ISPA_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  RidgeWs w = ridge_layout(workspace, n_layers, h);
+  w.R = linv;  // the forward solve of L Z = I runs in the caller's buffer
+  const int nblk = (h + kCholBlock - 1) / kCholBlock;
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  ISPA_TRY(ispa::launch_copy_add_diag(G, w.L, h, n_layers, lambda, s));
+  ISPA_TRY(cholesky(0, nblk, w, h, n_layers, info, s));
+  ISPA_TRY(ispa::launch_identity(linv, h, n_layers, s));
+  ISPA_TRY(solve_lower(0, nblk, w, h, n_layers, s));
+  // ||L^{-1}||_F^2 = tr((G + lambda I)^{-1}) -> (h - lambda tr) / n_warm
+  ISPA_TRY(ispa::launch_drift_sum(linv, h, h, h, hh, n_layers, w.part, h, lambda,
+                                  static_cast<double>(n_warm), nullptr, ref, s));
+  return ISPA_OK;
+}
+
+int ispa_drift_score(int n_layers, int h, const float* linv, const double* ref, const void* x,
+                     int64_t n_tok, int64_t stride, double* score, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  if (!linv || !ref || !x || !score) return ISPA_ERR_NULL;
+  if (n_layers < 1 || h < 1 || n_tok < 1 || stride < 1) return ISPA_ERR_SHAPE;
+  if (h % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  const int64_t n_s = (n_tok + stride - 1) / stride;
+  if (n_s > INT32_MAX) return ISPA_ERR_SHAPE;
+  if (!workspace || ws_bytes < ispa_drift_workspace_bytes(n_layers, h, n_s))
+    return ISPA_ERR_WORKSPACE;
+  if (!aligned16(linv) || !aligned16(ref) || !aligned16(x) || !aligned16(score) ||
+      !aligned16(workspace))
+    return ISPA_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  float* Y = static_cast<float*>(workspace);
+  double* part = reinterpret_cast<double*>(
+      static_cast<char*>(workspace) +
+      align_up(static_cast<size_t>(n_layers) * h * n_s * sizeof(float)));
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  // Y = L^{-1} X_s^T: column j is L^{-1} x^T for sampled token j * stride,
+  // so its squared norm is that token's leverage x (G + lambda I)^{-1} x^T
+  ISPA_TRY(gemm(h, static_cast<int>(n_s), h, linv, h, 1, hh, false, x, 1, stride * h,
+                n_tok * h, true, Y, n_s, h * n_s, 1.f, 0.f, n_layers, false, s));
+  ISPA_TRY(ispa::launch_drift_sum(Y, h, static_cast<int>(n_s), n_s, h * n_s, n_layers, part,
+                                  h, 0.0, static_cast<double>(n_s), ref, score, s));
+  return ISPA_OK;
+}
+
 int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in, int h_out,
                  void* stream) {
   if (!x || !w || !y) return ISPA_ERR_NULL;

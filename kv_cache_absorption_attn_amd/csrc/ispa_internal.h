@@ -106,6 +106,17 @@ size_t layer_score_partial_count(int n_layers, int h);
 hipError_t launch_apply_dw(int n_layers, int h, const int* selected, const float* dW,
                            uint16_t* Wo, hipStream_t stream);
 
+// ---------------------------------------------------------------- drift score
+hipError_t launch_identity(float* M, int h, int batch, hipStream_t stream);
+// Row blocks of the summed-squares reduction of a matrix with `rows` rows.
+int drift_partial_count(int rows);
+// Summed squares S of each rows x cols fp32 matrix A[b] (row stride ld,
+// matrix stride mat_stride), then out[b] = (h - lam S) / n_div when ref is
+// null, else (S / n_div) / ref[b]. partial: batch * drift_partial_count(rows).
+hipError_t launch_drift_sum(const float* A, int rows, int cols, int64_t ld, int64_t mat_stride,
+                            int batch, double* partial, double h, double lam, double n_div,
+                            const double* ref, double* out, hipStream_t stream);
+
 // ---------------------------------------------------------------- projection
 hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
                           int h_in, int h_out, hipStream_t stream);

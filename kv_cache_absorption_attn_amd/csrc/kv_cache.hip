@@ -359,6 +359,19 @@ int ispa_kv_evict_history(ispa_kv_cache* cache, int layer, void* stream) {
   return (ek == hipSuccess && ev == hipSuccess) ? ISPA_OK : ISPA_ERR_HIP;
 }
 
+int ispa_kv_restore_history(ispa_kv_cache* cache, int layer) {
+  if (!cache) return ISPA_ERR_NULL;
+  if (!valid_layer(cache, layer)) return ISPA_ERR_SHAPE;
+  LayerKV& L = cache->layers[layer];
+  // an L-layer writes slot 0: as a full-history layer at chunk 0 that slot is
+  // its current one and the history is empty
+  if (L.local_only) {
+    L.local_only = false;
+    L.chunk = 0;
+  }
+  return ISPA_OK;
+}
+
 const char* ispa_kv_last_error(const ispa_kv_cache* cache) {
   return cache ? cache->err.text : g_create_error.text;
 }

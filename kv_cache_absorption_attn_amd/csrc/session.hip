@@ -1,0 +1,280 @@
+// ISPA streaming session: the warmup -> absorption -> streaming life cycle of
+// all attention layers over one KV cache, with event-triggered
+// recalibration (ISPA paper §3.1 items 1-3, §3.3 including its last
+// paragraph). Host-side control only: every step is a call of the C ABI in
+// include/ispa.h, enqueued on the caller's stream. Contracts are in
+// include/ispa.h.
+//
+// Phases:
+//  warmup  every layer runs the dual-stream attention over sink + history +
+//          current (O_local, O_full, D), accumulates G, C, E and projects
+//          O_full through the original W; after t_warm chunks the session
+//          solves dW (against the original W), scores and selects K layers,
+//          writes bf16(W + dW) for them into the active weights, drops their
+//          history and prepares their drift state;
+//  stream  L-layers attend sink + current through W + dW, F-layers their
+//          whole history through W; each L-layer's local output gets a drift
+//          score, and when one exceeds the threshold the session re-enters
+//          warmup: L-layers get W back and restart their history, and the
+//          statistics start over.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "ispa.h"
+
+namespace {
+
+size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+struct Layout {
+  float *G, *C, *E, *dW, *linv;
+  void* ridge_ws;
+  size_t ridge_bytes;
+  void* drift_ws;
+  size_t drift_bytes;
+  uint16_t *x, *d, *o;
+  int *info, *info_drift, *selected;
+  double *eps_abs, *eps_rel, *ref, *score;
+  size_t bytes;
+};
+
+int64_t drift_sample(const ispa_session_config& c) {
+  return (c.n_cur + c.drift_stride - 1) / c.drift_stride;
+}
+
+Layout layout(const ispa_session_config& c, void* base) {
+  Layout w{};
+  const int L = c.n_layers;
+  const size_t h = static_cast<size_t>(c.n_heads) * c.head_dim;
+  const size_t hh = h * h * L * sizeof(float);
+  const size_t act = align_up(static_cast<size_t>(c.n_cur) * h * 2);
+  w.ridge_bytes = ispa_ridge_workspace_bytes(L, static_cast<int>(h));
+  w.drift_bytes = ispa_drift_workspace_bytes(1, static_cast<int>(h), drift_sample(c));
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* q = p ? p + off : nullptr;
+    off = align_up(off + n);
+    return q;
+  };
+  w.G = reinterpret_cast<float*>(take(hh));
+  w.C = reinterpret_cast<float*>(take(hh));
+  w.E = reinterpret_cast<float*>(take(hh));
+  w.dW = reinterpret_cast<float*>(take(hh));
+  w.linv = reinterpret_cast<float*>(take(hh));
+  w.ridge_ws = take(w.ridge_bytes);
+  w.drift_ws = take(w.drift_bytes);
+  w.x = reinterpret_cast<uint16_t*>(take(act));
+  w.d = reinterpret_cast<uint16_t*>(take(act));
+  w.o = reinterpret_cast<uint16_t*>(take(act));
+  w.info = reinterpret_cast<int*>(take(L * sizeof(int)));
+  w.info_drift = reinterpret_cast<int*>(take(L * sizeof(int)));
+  w.selected = reinterpret_cast<int*>(take(L * sizeof(int)));
+  w.eps_abs = reinterpret_cast<double*>(take(L * sizeof(double)));
+  w.eps_rel = reinterpret_cast<double*>(take(L * sizeof(double)));
+  w.ref = reinterpret_cast<double*>(take(L * sizeof(double)));
+  w.score = reinterpret_cast<double*>(take(L * sizeof(double)));
+  w.bytes = off;
+  return w;
+}
+
+bool valid_config(const ispa_session_config* c) {
+  return c->n_layers >= 1 && c->n_heads >= 1 && c->n_cur >= 1 && c->n_sink >= 0 &&
+         c->hist_capacity >= 0 && c->t_warm >= 1 && c->k_select >= 0 &&
+         c->k_select <= c->n_layers && c->drift_stride >= 1 && c->sm_scale > 0.f &&
+         c->lambda >= 0.f;
+}
+
+}  // namespace
+
+struct ispa_session {
+  ispa_session_config cfg{};
+  ispa_kv_cache* kv = nullptr;
+  const uint16_t* wo = nullptr;  // original weights (read only)
+  uint16_t* w = nullptr;         // active weights
+  Layout ws{};
+  int h = 0;
+  int64_t hh = 0;
+  int phase = ISPA_PHASE_WARMUP;
+  int warm_count = 0;
+  int64_t chunk = 0;
+  int n_calibrations = 0;
+  std::vector<int> is_local;     // host copy of the current selection
+  std::vector<double> eps_rel;   // host copy of the last errors
+  std::vector<double> score;     // host copy of the last drift scores
+};
+
+extern "C" {
+
+size_t ispa_session_workspace_bytes(const ispa_session_config* cfg) {
+  if (!cfg || !valid_config(cfg)) return 0;
+  return layout(*cfg, nullptr).bytes;
+}
+
+int ispa_session_create(const ispa_session_config* cfg, const void* wo, void* w_active,
+                        void* workspace, size_t ws_bytes, void* stream, ispa_session** out) {
+  if (!out) return ISPA_ERR_NULL;
+  *out = nullptr;
+  if (!cfg || !wo || !w_active || !workspace) return ISPA_ERR_NULL;
+  if (!valid_config(cfg)) return ISPA_ERR_SHAPE;
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return ISPA_ERR_UNSUPPORTED;
+  if (ws_bytes < layout(*cfg, nullptr).bytes) return ISPA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(wo) | reinterpret_cast<uintptr_t>(w_active) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15u)
+    return ISPA_ERR_ALIGN;
+  ispa_session* s = new (std::nothrow) ispa_session();
+  if (!s) return ISPA_ERR_HIP;
+  s->cfg = *cfg;
+  s->h = cfg->n_heads * cfg->head_dim;
+  s->hh = static_cast<int64_t>(s->h) * s->h;
+  s->wo = static_cast<const uint16_t*>(wo);
+  s->w = static_cast<uint16_t*>(w_active);
+  s->ws = layout(*cfg, workspace);
+  s->is_local.assign(cfg->n_layers, 0);
+  s->eps_rel.assign(cfg->n_layers, 0.0);
+  s->score.assign(cfg->n_layers, 0.0);
+  int st = ispa_kv_create(cfg->n_layers, cfg->n_heads, cfg->head_dim, cfg->n_sink, cfg->n_cur,
+                          cfg->hist_capacity, &s->kv);
+  if (st != ISPA_OK) {
+    delete s;
+    return st;
+  }
+  // the active weights start as the original ones
+  if (hipMemcpyAsync(s->w, s->wo, static_cast<size_t>(s->hh) * cfg->n_layers * 2,
+                     hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)) != hipSuccess) {
+    ispa_kv_destroy(s->kv);
+    delete s;
+    return ISPA_ERR_HIP;
+  }
+  *out = s;
+  return ISPA_OK;
+}
+
+int ispa_session_destroy(ispa_session* s) {
+  if (!s) return ISPA_ERR_NULL;
+  const int st = ispa_kv_destroy(s->kv);
+  delete s;
+  return st;
+}
+
+ispa_kv_cache* ispa_session_cache(ispa_session* s) { return s ? s->kv : nullptr; }
+
+int ispa_session_layer(ispa_session* s, int layer, const void* q, void* y, void* stream) {
+  if (!s || !q || !y) return ISPA_ERR_NULL;
+  const ispa_session_config& c = s->cfg;
+  if (layer < 0 || layer >= c.n_layers) return ISPA_ERR_SHAPE;
+  const uint16_t* wl = s->w + layer * s->hh;
+  if (s->phase == ISPA_PHASE_WARMUP) {
+    // dual stream: X = O_local and D into the statistics, O_full projected
+    int st = ispa_kv_attn(s->kv, layer, q, c.n_cur, c.sm_scale, s->ws.x, nullptr, nullptr,
+                          nullptr, s->ws.o, nullptr, s->ws.d, stream);
+    if (st != ISPA_OK) return st;
+    st = ispa_gram_accumulate(s->ws.x, s->ws.d, c.n_cur, s->h, 1, s->ws.G + layer * s->hh,
+                              s->ws.C + layer * s->hh, s->ws.E + layer * s->hh,
+                              s->warm_count == 0 ? 1 : 0, stream);
+    if (st != ISPA_OK) return st;
+    return ispa_project(s->ws.o, wl, y, c.n_cur, s->h, s->h, stream);
+  }
+  int st = ispa_kv_layer_forward(s->kv, layer, q, c.n_cur, c.sm_scale, wl, s->ws.x, y, stream);
+  if (st != ISPA_OK || !s->is_local[layer] || c.drift_threshold <= 0.0) return st;
+  return ispa_drift_score(1, s->h, s->ws.linv + layer * s->hh, s->ws.ref + layer, s->ws.x,
+                          c.n_cur, c.drift_stride, s->ws.score + layer, s->ws.drift_ws,
+                          s->ws.drift_bytes, stream);
+}
+
+int ispa_session_end_chunk(ispa_session* s, void* stream, int* event) {
+  if (!s) return ISPA_ERR_NULL;
+  const ispa_session_config& c = s->cfg;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int L = c.n_layers;
+  if (event) *event = ISPA_EVENT_NONE;
+  int st = ispa_kv_advance(s->kv);
+  if (st != ISPA_OK) return st;
+  ++s->chunk;
+  if (s->phase == ISPA_PHASE_WARMUP) {
+    if (++s->warm_count < c.t_warm) return ISPA_OK;
+    // transition: solve against the original W, score, select, update
+    st = ispa_ridge_solve(L, s->h, s->ws.G, s->ws.C, s->wo, c.lambda, s->ws.dW, s->ws.info,
+                          s->ws.ridge_ws, s->ws.ridge_bytes, stream);
+    if (st == ISPA_OK)
+      st = ispa_layer_score(L, s->h, s->ws.G, s->ws.C, s->ws.E, s->wo, s->ws.dW, c.lambda,
+                            s->ws.info, c.k_select, s->ws.ridge_ws, s->ws.ridge_bytes,
+                            s->ws.eps_abs, s->ws.eps_rel, s->ws.selected, stream);
+    if (st == ISPA_OK && hipMemcpyAsync(s->w, s->wo, static_cast<size_t>(s->hh) * L * 2,
+                                        hipMemcpyDeviceToDevice, hs) != hipSuccess)
+      st = ISPA_ERR_HIP;
+    if (st == ISPA_OK) st = ispa_apply_dW(L, s->h, s->ws.selected, s->ws.dW, s->w, stream);
+    if (st == ISPA_OK && c.drift_threshold > 0.0)
+      st = ispa_drift_prepare(L, s->h, s->ws.G, c.lambda, c.n_cur * c.t_warm, s->ws.linv,
+                              s->ws.ref, s->ws.info_drift, s->ws.ridge_ws, s->ws.ridge_bytes,
+                              stream);
+    if (st != ISPA_OK) return st;
+    // which layers turn local is a host decision: their history is freed
+    std::vector<int> sel(L);
+    if (hipMemcpyAsync(sel.data(), s->ws.selected, L * sizeof(int), hipMemcpyDeviceToHost, hs) !=
+            hipSuccess ||
+        hipMemcpyAsync(s->eps_rel.data(), s->ws.eps_rel, L * sizeof(double),
+                       hipMemcpyDeviceToHost, hs) != hipSuccess ||
+        hipStreamSynchronize(hs) != hipSuccess)
+      return ISPA_ERR_HIP;
+    for (int l = 0; l < L; ++l) {
+      s->is_local[l] = sel[l] ? 1 : 0;
+      s->score[l] = 0.0;
+      if (sel[l] && (st = ispa_kv_evict_history(s->kv, l, stream)) != ISPA_OK) return st;
+    }
+    s->phase = ISPA_PHASE_STREAM;
+    ++s->n_calibrations;
+    if (event) *event = ISPA_EVENT_ABSORBED;
+    return ISPA_OK;
+  }
+  if (c.drift_threshold <= 0.0) return ISPA_OK;
+  // drift check of the L-layers of the chunk just run
+  if (hipMemcpyAsync(s->score.data(), s->ws.score, L * sizeof(double), hipMemcpyDeviceToHost,
+                     hs) != hipSuccess ||
+      hipStreamSynchronize(hs) != hipSuccess)
+    return ISPA_ERR_HIP;
+  bool trigger = false;
+  for (int l = 0; l < L; ++l) {
+    if (!s->is_local[l]) {
+      s->score[l] = 0.0;
+      continue;
+    }
+    // NaN (a failed factor) counts as drift
+    if (!(s->score[l] <= c.drift_threshold)) trigger = true;
+  }
+  if (!trigger) return ISPA_OK;
+  // recalibration: L-layers get W back and restart their history; the
+  // statistics start over with the next chunk
+  for (int l = 0; l < L; ++l)
+    if (s->is_local[l] && (st = ispa_kv_restore_history(s->kv, l)) != ISPA_OK) return st;
+  if (hipMemcpyAsync(s->w, s->wo, static_cast<size_t>(s->hh) * L * 2, hipMemcpyDeviceToDevice,
+                     hs) != hipSuccess)
+    return ISPA_ERR_HIP;
+  std::fill(s->is_local.begin(), s->is_local.end(), 0);
+  s->phase = ISPA_PHASE_WARMUP;
+  s->warm_count = 0;
+  if (event) *event = ISPA_EVENT_RECALIBRATE;
+  return ISPA_OK;
+}
+
+int ispa_session_query(const ispa_session* s, ispa_session_state* out, int* is_local,
+                       double* eps_rel, double* drift) {
+  if (!s || !out) return ISPA_ERR_NULL;
+  out->phase = s->phase;
+  out->warm_count = s->warm_count;
+  out->n_calibrations = s->n_calibrations;
+  out->chunk = s->chunk;
+  const int L = s->cfg.n_layers;
+  for (int l = 0; l < L; ++l) {
+    if (is_local) is_local[l] = s->is_local[l];
+    if (eps_rel) eps_rel[l] = s->eps_rel[l];
+    if (drift) drift[l] = s->score[l];
+  }
+  return ISPA_OK;
+}
+
+}  // extern "C"

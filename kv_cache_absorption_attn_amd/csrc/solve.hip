@@ -268,7 +268,75 @@ __global__ void apply_dw_kernel(const int* __restrict__ selected, const float* _
   *wp = o;
 }
 
+// ---------------------------------------------------------------- drift score
+// (event-triggered recalibration, ISPA paper §3.3 last paragraph)
+
+// Identity of order h in each [h, h] fp32 matrix of the batch (grid.y).
+__global__ void identity_kernel(float* __restrict__ M, int h, int64_t hh) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= hh) return;
+  M[blockIdx.y * hh + i] = (i / h == i % h) ? 1.f : 0.f;
+}
+
+// Per (matrix, block of rows) fp64 partial sums of squares of a rows x cols
+// fp32 matrix (row stride ld), in a fixed order.
+__global__ __launch_bounds__(256) void sumsq_kernel(const float* __restrict__ A, int rows,
+                                                    int cols, int64_t ld, int64_t mat_stride,
+                                                    int rows_per_block,
+                                                    double* __restrict__ partial) {
+  __shared__ double red[4];
+  const float* Al = A + blockIdx.y * mat_stride;
+  const int r0 = blockIdx.x * rows_per_block;
+  const int r1 = min(rows, r0 + rows_per_block);
+  double s = 0.0;
+  for (int r = r0; r < r1; ++r)
+    for (int c = threadIdx.x; c < cols; c += blockDim.x) {
+      const double v = Al[static_cast<int64_t>(r) * ld + c];
+      s += v * v;
+    }
+  const double t = block_sum(s, red);
+  if (threadIdx.x == 0) partial[static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x] = t;
+}
+
+// With S = the summed squares of matrix l:
+//   reference (ref == null): out[l] = (h - lambda S) / n_warm, the expected
+//     leverage tr((G + lambda I)^{-1} G) / N with S = ||L^{-1}||_F^2 =
+//     tr((G + lambda I)^{-1});
+//   score: out[l] = (S / n_sample) / ref[l], S = sum of the sample's
+//     leverages ||L^{-1} x^T||^2.
+__global__ void drift_finalize_kernel(const double* __restrict__ partial, int nblk, int n_layers,
+                                      double h, double lam, double n_div,
+                                      const double* __restrict__ ref, double* __restrict__ out) {
+  for (int l = threadIdx.x; l < n_layers; l += blockDim.x) {
+    double S = 0.0;
+    for (int i = 0; i < nblk; ++i) S += partial[static_cast<int64_t>(l) * nblk + i];
+    out[l] = ref ? (S / n_div) / ref[l] : (h - lam * S) / n_div;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_identity(float* M, int h, int batch, hipStream_t stream) {
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  hipLaunchKernelGGL(identity_kernel, dim3(static_cast<unsigned>((hh + 255) / 256), batch),
+                     dim3(256), 0, stream, M, h, hh);
+  return hipGetLastError();
+}
+
+int drift_partial_count(int rows) { return (rows + kNB - 1) / kNB; }
+
+hipError_t launch_drift_sum(const float* A, int rows, int cols, int64_t ld, int64_t mat_stride,
+                            int batch, double* partial, double h, double lam, double n_div,
+                            const double* ref, double* out, hipStream_t stream) {
+  const int nblk = drift_partial_count(rows);
+  hipLaunchKernelGGL(sumsq_kernel, dim3(nblk, batch), dim3(256), 0, stream, A, rows, cols, ld,
+                     mat_stride, kNB, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(drift_finalize_kernel, dim3(1), dim3(256), 0, stream, partial, nblk, batch,
+                     h, lam, n_div, ref, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_copy_add_diag(const float* G, float* L, int h, int batch, float lam,
                                 hipStream_t stream) {

@@ -144,3 +144,48 @@ def test_kv_cache_validation():
     assert L.ispa_kv_attn(None, 0, A, 4, 0.1, A, 0, 0, 0, 0, 0, 0, 0) == NULL
     assert L.ispa_kv_layer_forward(None, 0, A, 4, 0.1, A, A, A, 0) == NULL
     assert ct.sizeof(_lib.KVView) == 4 * 8 + 6 * 8 + 3 * 8 + 8 + 2 * 4
+
+
+def test_drift_and_session_validation():
+    """Argument checks of the drift score and the streaming session that
+    return before any HIP call."""
+    import ctypes as ct
+    L = _lib.lib
+    assert ispa.ispa_drift_workspace_bytes(0, 128, 16) == 0
+    need = ispa.ispa_drift_workspace_bytes(2, 128, 16)
+    assert need >= ispa.ispa_ridge_workspace_bytes(2, 128)
+    assert L.ispa_drift_prepare(2, 128, 0, 0.01, 10, A, A, A, A, need, 0) == NULL
+    assert L.ispa_drift_prepare(2, 128, A, -1.0, 10, A, A, A, A, need, 0) == SHAPE
+    assert L.ispa_drift_prepare(2, 128, A, 0.01, 0, A, A, A, A, need, 0) == SHAPE
+    assert L.ispa_drift_prepare(2, 100, A, 0.01, 10, A, A, A, A, need, 0) == UNSUP
+    assert L.ispa_drift_prepare(2, 128, A, 0.01, 10, A, A, A, A, 64, 0) == WS
+    assert L.ispa_drift_prepare(2, 128, MIS, 0.01, 10, A, A, A, A, need, 0) == ALIGN
+    assert L.ispa_drift_score(2, 128, A, A, 0, 16, 1, A, A, need, 0) == NULL
+    assert L.ispa_drift_score(2, 128, A, A, A, 0, 1, A, A, need, 0) == SHAPE
+    assert L.ispa_drift_score(2, 128, A, A, A, 16, 0, A, A, need, 0) == SHAPE
+    assert L.ispa_drift_score(2, 128, A, A, A, 4096, 1, A, A, need, 0) == WS  # 4096 samples
+    assert L.ispa_drift_score(2, 128, A, A, A, 16, 1, A, MIS, need, 0) == ALIGN
+    assert L.ispa_kv_restore_history(None, 0) == NULL
+
+    cfg = _lib.SessionConfig(2, 2, 64, 1, 2, 0, 8, 16, 64, 0.125, 0.01, 4.0, 4)
+    n = L.ispa_session_workspace_bytes(ct.byref(cfg))
+    assert n > 0
+    bad = _lib.SessionConfig(2, 2, 64, 3, 2, 0, 8, 16, 64, 0.125, 0.01, 4.0, 4)  # K > layers
+    assert L.ispa_session_workspace_bytes(ct.byref(bad)) == 0
+    h = ct.c_void_p()
+    assert L.ispa_session_create(ct.byref(cfg), A, A, A, n, 0, None) == NULL
+    assert L.ispa_session_create(ct.byref(cfg), 0, A, A, n, 0, ct.byref(h)) == NULL
+    assert L.ispa_session_create(ct.byref(bad), A, A, A, n, 0, ct.byref(h)) == SHAPE
+    d96 = _lib.SessionConfig(2, 2, 96, 1, 2, 0, 8, 16, 64, 0.125, 0.01, 4.0, 4)
+    assert L.ispa_session_create(ct.byref(d96), A, A, A, n, 0, ct.byref(h)) == UNSUP
+    assert L.ispa_session_create(ct.byref(cfg), A, A, A, n - 1, 0, ct.byref(h)) == WS
+    assert L.ispa_session_create(ct.byref(cfg), MIS, A, A, n, 0, ct.byref(h)) == ALIGN
+    assert h.value is None
+    st = _lib.SessionState()
+    assert L.ispa_session_destroy(None) == NULL
+    assert L.ispa_session_cache(None) is None
+    assert L.ispa_session_layer(None, 0, A, A, 0) == NULL
+    assert L.ispa_session_end_chunk(None, 0, None) == NULL
+    assert L.ispa_session_query(None, ct.byref(st), None, None, None) == NULL
+    assert ct.sizeof(_lib.SessionConfig) == 6 * 4 + 3 * 8 + 2 * 4 + 8 + 8
+    assert ct.sizeof(_lib.SessionState) == 4 * 4 + 8
