@@ -267,6 +267,66 @@ def stream_measure(ispa, w: wl.Workload, frames=(60, 120), reps: int = 2, seed: 
     return res
 
 
+def session_measure(ispa, w: wl.Workload, n_stream: int = 3, seed: int = 2):
+    """The 14B-class life cycle through the native streaming session
+    (ispa_session_*): a fresh stream of t_warm warmup chunks (every layer
+    dual-stream, Gram accumulation, projection), the transition (solve,
+    score, selection, update, eviction, drift factors), then n_stream
+    streaming chunks with the drift check of the L-layers on. Per chunk the
+    layer calls are timed with HIP events; end_chunk (which reads the
+    selection or the drift scores back, so it waits for the stream) with
+    the host clock. K/V writes are outside the timed regions."""
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    nh, d, h, L = w.n_heads, w.head_dim, w.hidden, w.n_layers
+
+    def rnd(*shape, std=w.qkv_std):
+        return (torch.randn(*shape, generator=g, device=dev) * std).to(bf)
+
+    wo = rnd(L, h, h, std=w.wo_std)
+    q = [rnd(w.n_cur, nh, d) for _ in range(L)]
+    k_sink, v_sink = rnd(w.n_sink, nh, d), rnd(w.n_sink, nh, d)
+    k_chunk, v_chunk = rnd(w.n_cur, nh, d), rnd(w.n_cur, nh, d)
+    y = torch.empty(w.n_cur, h, dtype=bf, device=dev)
+    t_warm = w.n_steps
+    n_chunks = t_warm + n_stream
+    sess = ispa.Session(wo, n_heads=nh, head_dim=d, n_sink=w.n_sink, n_cur=w.n_cur,
+                        hist_capacity=n_chunks * w.n_cur, k_select=w.k_select, t_warm=t_warm,
+                        sm_scale=w.sm_scale, lam=w.lam, drift_threshold=1e30, drift_stride=16)
+    res = {"t_warm": t_warm, "warmup_chunk_ms": [], "stream_chunk_ms": [], "events": [],
+           "end_chunk_host_ms": [], "workspace_gb": round(sess.workspace.numel() / 1e9, 2)}
+    try:
+        for l in range(L):
+            sess.cache.write(l, k_sink, v_sink, sink=True)
+        for c in range(n_chunks):
+            for l in range(L):
+                sess.cache.write(l, k_chunk, v_chunk)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(L):
+                sess.layer(l, q[l], y)
+            e1.record()
+            t0 = time.perf_counter()
+            ev = sess.end_chunk()
+            torch.cuda.synchronize()
+            t_end = (time.perf_counter() - t0) * 1e3
+            ms = e0.elapsed_time(e1)
+            res["warmup_chunk_ms" if c < t_warm else "stream_chunk_ms"].append(round(ms, 2))
+            res["events"].append(ev)
+            res["end_chunk_host_ms"].append(round(t_end, 2))
+            print(f"[bench] session chunk {c}: layers {ms:.1f} ms, end_chunk {t_end:.1f} ms, "
+                  f"event {ev}", file=sys.stderr, flush=True)
+        st, loc, eps, drift = sess.state()
+        res["l_layers"] = sum(loc)
+        res["drift_scores_l_layers"] = [round(x, 3) for x, on in zip(drift, loc) if on][:4]
+        res["kv_gb"] = round(sess.cache.resident_bytes() / 1e9, 2)
+    finally:
+        sess.close()
+    return res
+
+
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -585,6 +645,8 @@ def main():
         del inp, ws, timing
         torch.cuda.empty_cache()
         out["stream"] = stream_measure(ispa, w)
+        torch.cuda.empty_cache()
+        out["session"] = session_measure(ispa, w)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_rows)

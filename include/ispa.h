@@ -199,7 +199,8 @@ int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in,
  *   workspace: ispa_ridge_workspace_bytes(n_layers, h) bytes at least.
  * ispa_drift_score: x [n_layers][n_tok, h] bf16; the sample is the rows
  *   0, stride, 2 stride, ... (ceil(n_tok / stride) of them); score
- *   [n_layers] fp64 out (+inf when ref is 0). workspace:
+ *   [n_layers] fp64 out (+inf when ref is 0); ref and score need only
+ *   8-byte alignment (one layer's entry may be passed alone). workspace:
  *   ispa_drift_workspace_bytes(n_layers, h, ceil(n_tok / stride)) bytes.
  * ispa_drift_workspace_bytes covers both calls (0 for invalid sizes).
  * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (sizes < 1, lambda < 0 or not

@@ -408,7 +408,10 @@ int ispa_drift_score(int n_layers, int h, const float* linv, const double* ref, 
   if (n_s > INT32_MAX) return ISPA_ERR_SHAPE;
   if (!workspace || ws_bytes < ispa_drift_workspace_bytes(n_layers, h, n_s))
     return ISPA_ERR_WORKSPACE;
-  if (!aligned16(linv) || !aligned16(ref) || !aligned16(x) || !aligned16(score) ||
+  // ref and score are read and written per element: 8-byte alignment, so a
+  // layer's entry of a per-layer vector can be passed on its own
+  const auto aligned8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; };
+  if (!aligned16(linv) || !aligned8(ref) || !aligned16(x) || !aligned8(score) ||
       !aligned16(workspace))
     return ISPA_ERR_ALIGN;
   const hipStream_t s = as_stream(stream);

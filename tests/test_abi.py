@@ -165,6 +165,7 @@ def test_drift_and_session_validation():
     assert L.ispa_drift_score(2, 128, A, A, A, 16, 0, A, A, need, 0) == SHAPE
     assert L.ispa_drift_score(2, 128, A, A, A, 4096, 1, A, A, need, 0) == WS  # 4096 samples
     assert L.ispa_drift_score(2, 128, A, A, A, 16, 1, A, MIS, need, 0) == ALIGN
+    assert L.ispa_drift_score(2, 128, A, A + 4, A, 16, 1, A, A, need, 0) == ALIGN  # ref: 8 B
     assert L.ispa_kv_restore_history(None, 0) == NULL
 
     cfg = _lib.SessionConfig(2, 2, 64, 1, 2, 0, 8, 16, 64, 0.125, 0.01, 4.0, 4)

@@ -144,7 +144,9 @@ class OracleSession:
 
 
 def test_session_life_cycle_with_recalibration():
-    """Three layers (query temperatures 0.5, 1, 2 separate their errors),
+    """Three layers (query temperatures 1, 0.5, 2 separate their errors; the
+    absorbed layer is layer 1, whose per-layer entries sit off 16-byte
+    boundaries),
     2 warmup chunks, K = 1, drift threshold 4. The stream is temporally
     coherent: a chunk's K, V and Q are its scene's tensors plus small
     per-chunk noise. Chunks 0-1 warm up, 2-3 stream in the same scene,
@@ -154,7 +156,7 @@ def test_session_life_cycle_with_recalibration():
     L, nh, d, ns, nc = 3, 2, 64, 64, 256
     h = nh * d
     scale, lam, K, t_warm, tau = 1.0 / np.sqrt(d), 1e-2, 1, 2, 4.0
-    temps = [0.5, 1.0, 2.0]
+    temps = [1.0, 0.5, 2.0]
     n_chunks, shift_at = 8, 4
     rnd = lambda shape, seed, std=1.0: wl.random_bf16(shape, std, 5000 + seed)
     ks = [rnd((ns, nh, d), 10 * l + 1) for l in range(L)]
