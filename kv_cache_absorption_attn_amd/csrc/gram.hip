@@ -424,6 +424,7 @@ hipError_t launch_gram(const GramParams& p, hipStream_t stream) {
 
 hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, int h_in,
                           int h_out, hipStream_t stream) {
+  if (nt_gemm256_supported(h_in)) return launch_nt_gemm256_bf16(x, w, y, n, h_in, h_out, stream);
   const int64_t tiles = ((n + kT - 1) / kT) * ((h_out + kT - 1) / kT);
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL(nt_gemm_kernel<false>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
@@ -438,6 +439,7 @@ hipError_t launch_split_nt_gemm_f32(const float* c, uint16_t* hi, uint16_t* lo,
   const int64_t count = hh * batch;
   if (count == 0) return hipSuccess;
   hipLaunchKernelGGL(split_bf16_kernel, dim3(4096), dim3(256), 0, stream, c, hi, lo, count);
+  if (nt_gemm256_supported(h)) return launch_nt_gemm256_split_f32(hi, lo, w, y, h, batch, stream);
   const int64_t tiles = static_cast<int64_t>((h + kT - 1) / kT) * ((h + kT - 1) / kT);
   hipLaunchKernelGGL(nt_gemm_kernel<true>, dim3(static_cast<unsigned>(tiles), batch),
                      dim3(kThreads), 0, stream, hi, lo, hh, w, hh, static_cast<void*>(y), hh,

@@ -118,6 +118,12 @@ hipError_t launch_drift_sum(const float* A, int rows, int cols, int64_t ld, int6
                             const double* ref, double* out, hipStream_t stream);
 
 // ---------------------------------------------------------------- projection
+// The 256 x 128-tile NT GEMM (contraction length a multiple of 32).
+bool nt_gemm256_supported(int h_in);
+hipError_t launch_nt_gemm256_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
+                                  int h_in, int h_out, hipStream_t stream);
+hipError_t launch_nt_gemm256_split_f32(const uint16_t* hi, const uint16_t* lo, const uint16_t* w,
+                                       float* y, int h, int batch, hipStream_t stream);
 hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
                           int h_in, int h_out, hipStream_t stream);
 

@@ -1,0 +1,254 @@
+// NT GEMM on bf16 matrix cores, fp32 accumulate, for the L-layer output
+// projection Y = X W^T (ISPA paper §3.1 item 3) and the C W_o product of the
+// closed-form absorb (§3.2): Y[m][o] = sum_k A[m][k] W[o][k], both operands
+// k-contiguous. Used when the contraction length is a multiple of 32.
+//
+// Workgroup tile 256 (m) x 128 (o), 8 waves of 64 x 64 (2 x 2 blocks of
+// 32x32x16 MFMAs, 64 accumulators a lane). Arithmetic intensity
+// 2*256*128*32 FLOP per 24 KB staged = 85 FLOP/B, against 64 for 128 x 128
+// tiles, so the L2 -> CU operand stream stays well under the CU's load
+// bandwidth at the MFMA rate this kernel reaches.
+//
+// k-stages of 32 go through a 4-slot LDS ring filled by direct-to-LDS buffer
+// loads issued three stages ahead: each wave waits for its own loads of the
+// stage it is about to read (vmcnt), one barrier per stage publishes them and
+// frees the slot that the next issue overwrites. A row's 16-byte chunk c
+// (k = 8c .. 8c+7 of the stage) is stored at chunk position c ^ ((r >> 2) & 3)
+// of its 64-byte LDS row, so the 16 rows of one quarter-wave's 16-byte
+// fragment reads cover all 64 banks once. Rows past the matrix re-load its
+// last row (their results are never stored).
+
+#include "device_common.h"
+#include "ispa_internal.h"
+
+namespace ispa {
+namespace {
+
+constexpr int kBM = 256, kBN = 128, kBK = 32;
+constexpr int kNtThreads = 512;
+constexpr int kRowE = kBK;                 // bf16 elements per LDS row (64 bytes)
+constexpr int kGroupM = 8;                 // row tiles per L2 group
+
+__device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// 16 bytes of row `row` (chunk position `pos`) of a stage slot.
+__device__ __forceinline__ bf16x8 frag(const uint16_t* slot, int row, int pos) {
+  return *reinterpret_cast<const bf16x8*>(slot + row * kRowE + 8 * pos);
+}
+
+// Buffer descriptor of a raw (untyped) range from `base`: the same four
+// dwords as raw_rsrc, as plain SGPRs for the asm load below.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 desc_of(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 d;
+  d.x = static_cast<uint32_t>(a);
+  d.y = static_cast<uint32_t>(a >> 32) & 0xFFFFu;  // stride 0
+  d.z = 0x7fffffffu;                               // no practical range limit
+  d.w = 0x00020000u;                               // 32-bit data format
+  return d;
+}
+
+// Direct-to-LDS 16-byte load (lane l's 16 bytes at voff + soff land at
+// lds + 16 l) written in asm, so the compiler does not track it: with the
+// builtin, its wait-count pass keeps the prologue's loads into slot 0 pending
+// at the loop head and drains every load in flight once per ring turn. The
+// waits are explicit instead (vmcnt before each stage's barrier). No VGPR is
+// written by the load (its data goes to LDS); one wait state separates the
+// M0 write from its use.
+__device__ __forceinline__ void dma16(const u32x4& d, uint16_t* lds, uint32_t voff, int soff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ISPA_LDS(void, lds))));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(m0v), "v"(voff), "s"(d), "s"(soff)
+      : "memory", "m0");
+}
+
+struct NtArgs {
+  const uint16_t* a;   // [batch][n, h_in] bf16
+  const uint16_t* a2;  // second plane of A (or null): the contraction runs over both
+  int64_t a_bs;
+  const uint16_t* w;   // [batch][h_out, h_in] bf16
+  int64_t w_bs;
+  void* y;             // [batch][n, h_out], bf16 or fp32
+  int64_t y_bs;
+  int64_t n;
+  int h_in, h_out;
+};
+
+template <bool F32OUT>
+__global__ __launch_bounds__(kNtThreads, 1) void nt_gemm256_kernel(const NtArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa0[kBM * kRowE], sa1[kBM * kRowE],
+      sa2[kBM * kRowE], sa3[kBM * kRowE];
+  __shared__ __attribute__((aligned(16))) uint16_t sb0[kBN * kRowE], sb1[kBN * kRowE],
+      sb2[kBN * kRowE], sb3[kBN * kRowE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, l32 = lane % 32, hf = lane / 32;
+  const int wm = wave / 2, wn = wave % 2;
+  const int tiles_m = static_cast<int>((p.n + kBM - 1) / kBM);
+  const int tiles_n = (p.h_out + kBN - 1) / kBN;
+  // grouped order: kGroupM row tiles share each column panel of W in L2
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_group = kGroupM * tiles_n;
+  const int g = t / per_group, first_m = g * kGroupM;
+  const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int tm = first_m + (t % per_group) % gm, tn = (t % per_group) / gm;
+  const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+  const int n0 = tn * kBN;
+  const int64_t b = blockIdx.y;
+
+  const int nk = p.h_in / kBK;
+  const int nst = p.a2 ? 2 * nk : nk;
+  const u32x4 ra1 = desc_of(p.a + b * p.a_bs);
+  const u32x4 ra2 = desc_of((p.a2 ? p.a2 : p.a) + b * p.a_bs);
+  const u32x4 rw = desc_of(p.w + b * p.w_bs);
+
+  // per-lane byte offsets of this wave's loads: A rows wave*32 + 16j + lane/4,
+  // B rows wave*16 + lane/4; the stage's k offset goes in the scalar offset
+  uint32_t va[2], vb;
+  {
+    const int p4 = lane % 4;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = wave * 32 + 16 * j + lane / 4;
+      int64_t gr = m0 + row;
+      if (gr > p.n - 1) gr = p.n - 1;
+      va[j] = static_cast<uint32_t>((gr * p.h_in + 8 * chunk_pos(row, p4)) * 2);
+    }
+    const int row = wave * 16 + lane / 4;
+    int gr = n0 + row;
+    if (gr > p.h_out - 1) gr = p.h_out - 1;
+    vb = static_cast<uint32_t>((static_cast<int64_t>(gr) * p.h_in + 8 * chunk_pos(row, p4)) * 2);
+  }
+  auto issue = [&](int s, uint16_t* da, uint16_t* db) {
+    const bool second = s >= nk;
+    const int soff = (second ? s - nk : s) * kBK * 2;
+    const auto r = second ? ra2 : ra1;
+    dma16(r, da + (wave * 32) * kRowE, va[0], soff);
+    dma16(r, da + (wave * 32 + 16) * kRowE, va[1], soff);
+    dma16(rw, db + (wave * 16) * kRowE, vb, soff);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  // fragment rows and the chunk positions of this lane's two k-steps
+  int ar[2], br[2], apos[2][2], bpos[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    ar[i] = wm * 64 + i * 32 + l32;
+    br[i] = wn * 64 + i * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      apos[i][kk] = chunk_pos(ar[i], 2 * kk + hf);
+      bpos[i][kk] = chunk_pos(br[i], 2 * kk + hf);
+    }
+  }
+
+  if (nst > 0) issue(0, sa0, sb0);
+  if (nst > 1) issue(1, sa1, sb1);
+  if (nst > 2) issue(2, sa2, sb2);
+
+  // one stage: wait for its data, publish, refill the slot freed by the
+  // previous stage, then 2 k-steps of 4 MFMAs
+  auto stage = [&](int s, const uint16_t* __restrict__ ca, const uint16_t* __restrict__ cb,
+                   uint16_t* __restrict__ na, uint16_t* __restrict__ nb)
+      __attribute__((always_inline)) {
+    if (s + 2 < nst)
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if (s + 1 < nst)
+      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // a plain barrier: __syncthreads() would add a workgroup fence, i.e. a
+    // wait for every load in flight, including the two stages issued ahead
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // both k-steps' fragments at once; the refill loads go out between the
+    // first k-step's MFMAs, whose issue would otherwise leave the wave idle
+    bf16x8 av[2][2], bv[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        av[kk][i] = frag(ca, ar[i], apos[i][kk]);
+        bv[kk][i] = frag(cb, br[i], bpos[i][kk]);
+      }
+    const bool refill = s + 3 < nst;
+    const bool second = s + 3 >= nk;
+    const int soff = (second ? s + 3 - nk : s + 3) * kBK * 2;
+    const u32x4 rsa = second ? ra2 : ra1;
+    acc[0][0] = mfma32x32x16(av[0][0], bv[0][0], acc[0][0]);
+    if (refill) dma16(rsa, na + (wave * 32) * kRowE, va[0], soff);
+    acc[0][1] = mfma32x32x16(av[0][0], bv[0][1], acc[0][1]);
+    if (refill) dma16(rsa, na + (wave * 32 + 16) * kRowE, va[1], soff);
+    acc[1][0] = mfma32x32x16(av[0][1], bv[0][0], acc[1][0]);
+    if (refill) dma16(rw, nb + (wave * 16) * kRowE, vb, soff);
+    acc[1][1] = mfma32x32x16(av[0][1], bv[0][1], acc[1][1]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(av[1][i], bv[1][j], acc[i][j]);
+  };
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+    stage(s0, sa0, sb0, sa3, sb3);
+    if (s0 + 1 < nst) stage(s0 + 1, sa1, sb1, sa0, sb0);
+    if (s0 + 2 < nst) stage(s0 + 2, sa2, sb2, sa1, sb1);
+    if (s0 + 3 < nst) stage(s0 + 3, sa3, sb3, sa2, sb2);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int o = n0 + wn * 64 + j * 32 + l32;
+      if (o >= p.h_out) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+        if (m >= p.n) continue;
+        if constexpr (F32OUT)
+          static_cast<float*>(p.y)[b * p.y_bs + m * p.h_out + o] = acc[i][j][r];
+        else
+          static_cast<uint16_t*>(p.y)[b * p.y_bs + m * p.h_out + o] =
+              f32_to_bf16_bits(acc[i][j][r]);
+      }
+    }
+  }
+}
+
+template <bool F32OUT>
+hipError_t launch_nt(const NtArgs& a, int batch, hipStream_t stream) {
+  const int64_t tiles = ((a.n + kBM - 1) / kBM) * ((a.h_out + kBN - 1) / kBN);
+  if (tiles == 0 || batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(nt_gemm256_kernel<F32OUT>, dim3(static_cast<unsigned>(tiles), batch),
+                     dim3(kNtThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool nt_gemm256_supported(int h_in) { return h_in > 0 && h_in % kBK == 0; }
+
+hipError_t launch_nt_gemm256_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
+                                  int h_in, int h_out, hipStream_t stream) {
+  NtArgs a{x, nullptr, 0, w, 0, y, 0, n, h_in, h_out};
+  return launch_nt<false>(a, 1, stream);
+}
+
+hipError_t launch_nt_gemm256_split_f32(const uint16_t* hi, const uint16_t* lo, const uint16_t* w,
+                                       float* y, int h, int batch, hipStream_t stream) {
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  NtArgs a{hi, lo, hh, w, hh, y, hh, static_cast<int64_t>(h), h, h};
+  return launch_nt<true>(a, batch, stream);
+}
+
+}  // namespace ispa
