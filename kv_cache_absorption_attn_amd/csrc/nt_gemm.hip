@@ -53,10 +53,10 @@ __device__ __forceinline__ u32x4 desc_of(const void* base) {
 // lds + 16 l) written in asm, so the compiler does not track it: with the
 // builtin, its wait-count pass keeps the prologue's loads into slot 0 pending
 // at the loop head and drains every load in flight once per ring turn. The
-// waits are explicit instead (vmcnt before each stage's barrier). No VGPR is
-// written by the load (its data goes to LDS); one wait state separates the
-// M0 write from its use.
-__device__ __forceinline__ void dma16(const u32x4& d, uint16_t* lds, uint32_t voff, int soff) {
+// waits are explicit instead (vmcnt before each stage's barrier), and memory
+// clobbers keep the LDS reads below them. No VGPR is written by the load (its data
+// goes to LDS); one wait state separates the M0 write from its use.
+__device__ __forceinline__ void dma16_asm(const u32x4& d, uint16_t* lds, uint32_t voff, int soff) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ISPA_LDS(void, lds))));
   asm volatile(
@@ -129,9 +129,9 @@ __global__ __launch_bounds__(kNtThreads, 1) void nt_gemm256_kernel(const NtArgs 
     const bool second = s >= nk;
     const int soff = (second ? s - nk : s) * kBK * 2;
     const auto r = second ? ra2 : ra1;
-    dma16(r, da + (wave * 32) * kRowE, va[0], soff);
-    dma16(r, da + (wave * 32 + 16) * kRowE, va[1], soff);
-    dma16(rw, db + (wave * 16) * kRowE, vb, soff);
+    dma16_asm(r, da + (wave * 32) * kRowE, va[0], soff);
+    dma16_asm(r, da + (wave * 32 + 16) * kRowE, va[1], soff);
+    dma16_asm(rw, db + (wave * 16) * kRowE, vb, soff);
   };
 
   f32x16 acc[2][2];
@@ -187,11 +187,11 @@ __global__ __launch_bounds__(kNtThreads, 1) void nt_gemm256_kernel(const NtArgs 
     const int soff = (second ? s + 3 - nk : s + 3) * kBK * 2;
     const u32x4 rsa = second ? ra2 : ra1;
     acc[0][0] = mfma32x32x16(av[0][0], bv[0][0], acc[0][0]);
-    if (refill) dma16(rsa, na + (wave * 32) * kRowE, va[0], soff);
+    if (refill) dma16_asm(rsa, na + (wave * 32) * kRowE, va[0], soff);
     acc[0][1] = mfma32x32x16(av[0][0], bv[0][1], acc[0][1]);
-    if (refill) dma16(rsa, na + (wave * 32 + 16) * kRowE, va[1], soff);
+    if (refill) dma16_asm(rsa, na + (wave * 32 + 16) * kRowE, va[1], soff);
     acc[1][0] = mfma32x32x16(av[0][1], bv[0][0], acc[1][0]);
-    if (refill) dma16(rw, nb + (wave * 16) * kRowE, vb, soff);
+    if (refill) dma16_asm(rw, nb + (wave * 16) * kRowE, vb, soff);
     acc[1][1] = mfma32x32x16(av[0][1], bv[0][1], acc[1][1]);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
