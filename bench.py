@@ -473,6 +473,19 @@ def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
         gf = gram_flops(w.n_q, w.hidden)
         lines.append(f"Gram launches: {len(gram)}, average {avg / 1e3:.1f} us for "
                      f"{gf / 1e9:.1f} GFLOP = {gf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
+    proj = [dt for _, n, dt in rows if "nt_gemm256_kernel<false>" in n]
+    if proj:
+        avg = sum(proj) / len(proj)
+        pf = 2.0 * w.n_q * w.hidden * w.hidden
+        lines.append(f"Output projections (post-absorption chunk): {len(proj)}, average "
+                     f"{avg / 1e3:.1f} us for {pf / 1e9:.1f} GFLOP = "
+                     f"{pf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
+    cw = [dt for _, n, dt in rows if "nt_gemm256_kernel<true>" in n]
+    if cw:
+        avg = sum(cw) / len(cw)
+        cf = 2.0 * 2.0 * w.n_layers * w.hidden ** 3  # two bf16 planes of C
+        lines.append(f"C W_o products (absorb, all layers, two bf16 planes of C): {len(cw)}, "
+                     f"average {avg / 1e3:.1f} us = {cf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
     return "\n".join(lines) + "\n"
 
 
