@@ -385,3 +385,76 @@ def drift_score(x: np.ndarray, g: np.ndarray, lam: float, n_warm: int) -> float:
     m = g + lam * np.eye(g.shape[0])
     lev = np.einsum("ij,ji->i", x, np.linalg.solve(m, x.T))
     return float(lev.mean() / drift_reference(g, lam, n_warm))
+
+
+# ---------------------------------------------------------------------------
+# W8A8 output projection (ISPA paper §4.4, "Compatibility with Post-Training
+# Quantization": 8-bit weights and activations for the linear layers; here
+# the L-layer's W + dW is quantized after the update is folded in). Format:
+# OCP 8-bit floating point E4M3 (the "fn" variant: bias 7, no infinities,
+# S.1111.111 is NaN, largest finite 448). Readings: per-output-channel
+# weight scales and per-token activation scales, each absmax / 448, with
+# round-to-nearest-even codes saturated at +-448; the scale and the scaled
+# value are formed in fp32 (as the kernel forms them), so both sides take
+# the same code decisions.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of E4M3 codes (uint8): sign, 4 exponent bits (bias 7) and 3
+    mantissa bits; exponent field 0 holds the subnormals m * 2^-9; code
+    0x7F / 0xFF is NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each value (ties to the even code), values beyond
+    +-448 saturated to +-448; NaN maps to 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.minimum(np.abs(x), E4M3_MAX)
+    # quantum of the binade holding ax: 2^(e-3) for normal values, 2^-9 below 2^-6
+    ex = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    q = np.where(ax < 2.0 ** -6, 2.0 ** -9, 2.0 ** (ex - 3))
+    n = ax / q
+    r = np.floor(n)
+    frac = n - r
+    r = np.where((frac > 0.5) | ((frac == 0.5) & (r % 2 == 1)), r + 1, r)
+    mag = r * q
+    # magnitude -> code: exponent field and mantissa field
+    e_f = np.where(mag < 2.0 ** -6, 0, np.floor(np.log2(np.where(mag > 0, mag, 1.0))) + 7)
+    m_f = np.where(e_f == 0, np.round(mag / 2.0 ** -9), np.round((mag / 2.0 ** (e_f - 7) - 1) * 8))
+    code = (e_f.astype(np.int64) << 3) | m_f.astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return np.where(np.isnan(x), 0x7F, code).astype(np.uint8)
+
+
+def quantize_rows(a):
+    """Per-row E4M3 quantization of a [rows, k] matrix: absmax a = max |row|
+    (fp32), scale = a / 448 and inv = 448 / a (fp32 divisions; both 0 for an
+    all-zero row), codes = e4m3(fp32(value * inv)). Returns (codes uint8,
+    scale float32)."""
+    a32 = np.asarray(a, dtype=np.float32)
+    amax = np.max(np.abs(a32), axis=1)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1))
+    scale = np.where(nz, safe / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
+    inv = np.where(nz, np.float32(E4M3_MAX) / safe, np.float32(0)).astype(np.float32)
+    scaled = (a32 * inv[:, None]).astype(np.float32)
+    return e4m3_encode(scaled), scale
+
+
+def project_w8a8(x, wq, w_scale) -> np.ndarray:
+    """W8A8 projection: the activations x [N, in] are quantized per token,
+    then Y[m][o] = s_x[m] s_w[o] sum_k dq(Xq[m][k]) dq(Wq[o][k]) (exact)."""
+    xq, x_scale = quantize_rows(x)
+    acc = e4m3_decode(xq) @ e4m3_decode(wq).T
+    return acc * np.asarray(x_scale, dtype=np.float64)[:, None] * \
+        np.asarray(w_scale, dtype=np.float64)[None, :]
