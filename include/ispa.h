@@ -181,6 +181,36 @@ int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in,
                  int h_out, void* stream);
 
 /*
+ * W8A8 output projection (§4.4, "Compatibility with Post-Training
+ * Quantization": 8-bit weights and activations for the linear layers; for an
+ * L-layer W + dW is quantized after ispa_apply_dW). Format: OCP 8-bit
+ * floating point E4M3 ("fn": bias 7, no infinities, 0x7F / 0xFF NaN,
+ * largest finite 448), one byte a code.
+ *
+ * ispa_quantize_fp8: per-row quantization of a [rows, k] bf16 matrix (k % 8
+ *   == 0): scale[r] = absmax_r / 448 (fp32; 0 for an all-zero row) and
+ *   q[r][c] = the E4M3 code nearest to fp32(a[r][c] * (448 / absmax_r)),
+ *   ties to even (both divisions correctly rounded fp32). q [rows, k] uint8,
+ *   scale [rows] fp32. For weights, rows are output channels.
+ * ispa_project_w8a8: y [n, h_out] bf16 = X W^T with X = x [n, h_in] bf16
+ *   quantized per token the same way (into the workspace) and W given as
+ *   wq [h_out, h_in] E4M3 with w_scale [h_out]:
+ *     y[m][o] = s_x[m] s_w[o] sum_k dq(Xq[m][k]) dq(Wq[o][k]),
+ *   products exact, accumulated by the E4M3 matrix cores (their accumulation
+ *   keeps ~1e-4 of the sum of |products| at worst), scaled, rounded to
+ *   bf16. h_in % 64 == 0 and h_out % 8 == 0 (ISPA_ERR_UNSUPPORTED
+ *   otherwise). workspace: ispa_project_w8a8_workspace_bytes(n, h_in).
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE, ISPA_ERR_UNSUPPORTED,
+ *   ISPA_ERR_WORKSPACE, ISPA_ERR_ALIGN.
+ */
+int ispa_quantize_fp8(const void* a, int64_t rows, int k, void* q, float* scale,
+                      void* stream);
+size_t ispa_project_w8a8_workspace_bytes(int64_t n, int h_in);
+int ispa_project_w8a8(const void* x, const void* wq, const float* w_scale, void* y,
+                      int64_t n, int h_in, int h_out, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/*
  * Drift score for event-triggered recalibration (§3.3, last paragraph: on a
  * large scene transition or temporal distribution shift the warmup-to-
  * absorption procedure is re-entered; the pages give no trigger). For an

@@ -76,6 +76,12 @@ lib.ispa_kv_advance.restype = _i
 lib.ispa_kv_advance.argtypes = [_p]
 lib.ispa_kv_evict_history.restype = _i
 lib.ispa_kv_evict_history.argtypes = [_p, _i, _p]
+lib.ispa_quantize_fp8.restype = _i
+lib.ispa_quantize_fp8.argtypes = [_p, _i64, _i, _p, _p, _p]
+lib.ispa_project_w8a8_workspace_bytes.restype = _sz
+lib.ispa_project_w8a8_workspace_bytes.argtypes = [_i64, _i]
+lib.ispa_project_w8a8.restype = _i
+lib.ispa_project_w8a8.argtypes = [_p, _p, _p, _p, _i64, _i, _i, _p, _sz, _p]
 lib.ispa_kv_restore_history.restype = _i
 lib.ispa_kv_restore_history.argtypes = [_p, _i]
 lib.ispa_drift_workspace_bytes.restype = _sz
@@ -140,7 +146,8 @@ EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram
             "ispa_kv_layer_forward", "ispa_kv_restore_history", "ispa_drift_workspace_bytes",
             "ispa_drift_prepare", "ispa_drift_score", "ispa_session_workspace_bytes",
             "ispa_session_create", "ispa_session_destroy", "ispa_session_cache",
-            "ispa_session_layer", "ispa_session_end_chunk", "ispa_session_query")
+            "ispa_session_layer", "ispa_session_end_chunk", "ispa_session_query",
+            "ispa_quantize_fp8", "ispa_project_w8a8_workspace_bytes", "ispa_project_w8a8")
 
 
 class IspaError(RuntimeError):
@@ -499,3 +506,32 @@ class Session:
         _check("ispa_session_query", lib.ispa_session_query(
             self.handle, ct.byref(st), ct.cast(loc, _p), ct.cast(eps, _p), ct.cast(dr, _p)))
         return st, list(loc), list(eps), list(dr)
+
+
+def ispa_quantize_fp8(a, q, scale, *, stream=None) -> None:
+    """a [rows, k] bf16 -> q [rows, k] uint8 E4M3 codes, scale [rows] fp32."""
+    rows, k = a.shape
+    if tuple(q.shape) != (rows, k) or tuple(scale.shape) != (rows,):
+        raise ValueError("ispa_quantize_fp8: shape mismatch")
+    st = lib.ispa_quantize_fp8(_ptr(a, torch.bfloat16, "a"), rows, k, _ptr(q, torch.uint8, "q"),
+                               _ptr(scale, torch.float32, "scale"), _stream(stream))
+    _check("ispa_quantize_fp8", st)
+
+
+def ispa_project_w8a8_workspace_bytes(n: int, h_in: int) -> int:
+    return int(lib.ispa_project_w8a8_workspace_bytes(n, h_in))
+
+
+def ispa_project_w8a8(x, wq, w_scale, y, workspace, *, stream=None) -> None:
+    """y [n, h_out] bf16 = X W^T with X = x [n, h_in] bf16 quantized per
+    token and W = wq [h_out, h_in] E4M3 codes (uint8) with w_scale [h_out]."""
+    n, h_in = x.shape
+    h_out = wq.shape[0]
+    if wq.shape[1] != h_in or tuple(w_scale.shape) != (h_out,) or tuple(y.shape) != (n, h_out):
+        raise ValueError("ispa_project_w8a8: shape mismatch")
+    st = lib.ispa_project_w8a8(_ptr(x, torch.bfloat16, "x"), _ptr(wq, torch.uint8, "wq"),
+                               _ptr(w_scale, torch.float32, "w_scale"),
+                               _ptr(y, torch.bfloat16, "y"), n, h_in, h_out,
+                               _ptr(workspace, None, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ispa_project_w8a8", st)

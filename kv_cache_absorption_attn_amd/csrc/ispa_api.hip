@@ -429,6 +429,42 @@ int ispa_drift_score(int n_layers, int h, const float* linv, const double* ref, 
   return ISPA_OK;
 }
 
+int ispa_quantize_fp8(const void* a, int64_t rows, int k, void* q, float* scale,
+                      void* stream) {
+  if (!a || !q || !scale) return ISPA_ERR_NULL;
+  if (rows < 0 || k < 1 || rows > INT32_MAX) return ISPA_ERR_SHAPE;
+  if (k % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (!aligned16(a) || !aligned16(q) || !aligned16(scale)) return ISPA_ERR_ALIGN;
+  return hip_status(ispa::launch_quantize_rows_fp8(static_cast<const uint16_t*>(a), rows, k,
+                                                   static_cast<uint8_t*>(q), scale,
+                                                   as_stream(stream)));
+}
+
+size_t ispa_project_w8a8_workspace_bytes(int64_t n, int h_in) {
+  if (n < 0 || h_in < 1) return 0;
+  return align_up(static_cast<size_t>(n) * h_in) + align_up(static_cast<size_t>(n) * 4) + 256;
+}
+
+int ispa_project_w8a8(const void* x, const void* wq, const float* w_scale, void* y, int64_t n,
+                      int h_in, int h_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !wq || !w_scale || !y) return ISPA_ERR_NULL;
+  if (n < 0 || h_in < 1 || h_out < 1 || n > INT32_MAX) return ISPA_ERR_SHAPE;
+  if (h_in % 64 != 0 || h_out % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (n == 0) return ISPA_OK;
+  if (!workspace || ws_bytes < ispa_project_w8a8_workspace_bytes(n, h_in))
+    return ISPA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
+      !aligned16(workspace))
+    return ISPA_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(xq + align_up(static_cast<size_t>(n) * h_in));
+  ISPA_TRY(ispa::launch_quantize_rows_fp8(static_cast<const uint16_t*>(x), n, h_in, xq, sx, s));
+  return hip_status(ispa::launch_nt_gemm256_fp8(xq, sx, static_cast<const uint8_t*>(wq),
+                                                w_scale, static_cast<uint16_t*>(y), n, h_in,
+                                                h_out, s));
+}
+
 int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in, int h_out,
                  void* stream) {
   if (!x || !w || !y) return ISPA_ERR_NULL;

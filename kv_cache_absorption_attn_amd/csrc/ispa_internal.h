@@ -122,6 +122,15 @@ hipError_t launch_drift_sum(const float* A, int rows, int cols, int64_t ld, int6
 bool nt_gemm256_supported(int h_in);
 hipError_t launch_nt_gemm256_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
                                   int h_in, int h_out, hipStream_t stream);
+// E4M3 operands (contraction length a multiple of 64), scales per row of X
+// and per row of W, bf16 out.
+bool nt_gemm256_fp8_supported(int h_in);
+hipError_t launch_nt_gemm256_fp8(const uint8_t* xq, const float* sx, const uint8_t* wq,
+                                 const float* sw, uint16_t* y, int64_t n, int h_in, int h_out,
+                                 hipStream_t stream);
+// Per-row E4M3 quantization of a bf16 [rows, k] matrix (k % 8 == 0).
+hipError_t launch_quantize_rows_fp8(const uint16_t* a, int64_t rows, int k, uint8_t* q,
+                                    float* scale, hipStream_t stream);
 hipError_t launch_nt_gemm256_split_f32(const uint16_t* hi, const uint16_t* lo, const uint16_t* w,
                                        float* y, int h, int batch, hipStream_t stream);
 hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,

@@ -116,6 +116,30 @@ def test_score_apply_project_validation():
     assert p(A, A, A, 0, 128, 128, 0) == OK
 
 
+def test_w8a8_validation():
+    """Argument checks of the W8A8 calls that return before any launch."""
+    qz = _lib.lib.ispa_quantize_fp8
+    assert qz(A, 4, 64, 0, A, 0) == NULL
+    assert qz(A, -1, 64, A, A, 0) == SHAPE
+    assert qz(A, 4, 0, A, A, 0) == SHAPE
+    assert qz(A, 4, 60, A, A, 0) == UNSUP
+    assert qz(MIS, 4, 64, A, A, 0) == ALIGN
+    assert qz(A, 0, 64, A, A, 0) == OK
+    wsb = ispa.ispa_project_w8a8_workspace_bytes
+    assert wsb(-1, 64) == 0 and wsb(10, 0) == 0
+    need = wsb(100, 256)
+    assert need >= 100 * 256 + 100 * 4
+    pw = _lib.lib.ispa_project_w8a8
+    assert pw(A, A, 0, A, 100, 256, 128, A, need, 0) == NULL
+    assert pw(A, A, A, A, -1, 256, 128, A, need, 0) == SHAPE
+    assert pw(A, A, A, A, 100, 96, 128, A, need, 0) == UNSUP
+    assert pw(A, A, A, A, 100, 256, 100, A, need, 0) == UNSUP
+    assert pw(A, A, A, A, 100, 256, 128, A, need - 1, 0) == WS
+    assert pw(A, A, A, A, 100, 256, 128, 0, need, 0) == WS
+    assert pw(A, A, A, MIS, 100, 256, 128, A, need, 0) == ALIGN
+    assert pw(A, A, A, A, 0, 256, 128, 0, 0, 0) == OK
+
+
 def test_kv_cache_validation():
     """Argument checks of the streaming KV cache that return before any HIP
     call: bad shapes, NULL handles and NULL outputs."""
