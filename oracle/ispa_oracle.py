@@ -458,3 +458,90 @@ def project_w8a8(x, wq, w_scale) -> np.ndarray:
     acc = e4m3_decode(xq) @ e4m3_decode(wq).T
     return acc * np.asarray(x_scale, dtype=np.float64)[:, None] * \
         np.asarray(w_scale, dtype=np.float64)[None, :]
+
+
+# ---------------------------------------------------------------------------
+# Quantized decomposable attention (the ISPA paper's §3.4 builds on
+# FlashAttention-style LSE states and cites SageAttention's 8-bit attention;
+# §4.4 pairs ISPA with 8-bit quantization). Q K^T on E4M3 codes: each query
+# row (token, head) has its own scale; the keys are first smoothed by a
+# vector mu per head (subtracting the same vector from every key shifts all
+# of a query's scores by the same amount, so the softmax is unchanged and
+# only the LSE moves, by scale * q . mu, which is added back), then quantized
+# with one scale per head and per run of KEY_TILE keys from the start of
+# each KV segment. V, P and P V stay at bf16 precision.
+# ---------------------------------------------------------------------------
+
+KEY_TILE = 64
+
+
+def quantize_key_tiles(k, mu=None, tile: int = KEY_TILE):
+    """E4M3 quantization of one key segment k [n, nh, d] after smoothing:
+    r = fp32(k - mu) (mu [nh, d], the same for every key; None = 0), then for
+    each head and each run of `tile` keys from the segment start, the absmax
+    a of r over the run's tile x d values, scale = a / 448 and codes =
+    e4m3(fp32(r * (448 / a))) as in quantize_rows. Returns (codes [n, nh, d]
+    uint8, scales [n_tiles, nh] float32)."""
+    k32 = np.asarray(k, dtype=np.float32)
+    n, nh, d = k32.shape
+    m32 = np.zeros((nh, d), dtype=np.float32) if mu is None else \
+        np.asarray(mu, dtype=np.float32).reshape(nh, d)
+    r = (k32 - m32[None]).astype(np.float32)
+    n_tiles = (n + tile - 1) // tile
+    codes = np.zeros((n, nh, d), dtype=np.uint8)
+    scales = np.zeros((n_tiles, nh), dtype=np.float32)
+    for t in range(n_tiles):
+        blk = r[t * tile:(t + 1) * tile]                      # [rows, nh, d]
+        per_head = blk.transpose(1, 0, 2).reshape(nh, -1)     # one row per head
+        c, s = quantize_rows(per_head)
+        codes[t * tile:(t + 1) * tile] = c.reshape(nh, blk.shape[0], d).transpose(1, 0, 2)
+        scales[t] = s
+    return codes, scales
+
+
+def quantize_queries(q):
+    """Per-(token, head) E4M3 quantization of q [nq, nh, d]: codes [nq, nh, d],
+    scales [nh, nq] (the layout of the LSE outputs)."""
+    nq, nh, d = np.shape(q)
+    c, s = quantize_rows(np.asarray(q).reshape(nq * nh, d))
+    return c.reshape(nq, nh, d), s.reshape(nq, nh).T.copy()
+
+
+def dequantized_keys(k, mu=None, tile: int = KEY_TILE) -> np.ndarray:
+    """The smoothed keys as the quantized attention sees them: dq(codes) x the
+    scale of their tile and head (exact in fp64)."""
+    k = np.asarray(k)
+    if k.shape[0] == 0:
+        return np.zeros(k.shape, dtype=np.float64)
+    c, s = quantize_key_tiles(k, mu, tile)
+    per_row = np.repeat(s.astype(np.float64), tile, axis=0)[:k.shape[0]]
+    return e4m3_decode(c) * per_row[:, :, None]
+
+
+def key_mean(*segments) -> np.ndarray:
+    """Mean over all keys of the given segments [n_s, nh, d] -> [nh, d]
+    (fp64); a smoothing vector for quantize_key_tiles."""
+    ks = [np.asarray(k, dtype=np.float64) for k in segments if np.shape(k)[0] > 0]
+    allk = np.concatenate(ks, axis=0)
+    return allk.mean(axis=0)
+
+
+def decomposable_attention_fp8(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist,
+                               scale: float, mu=None) -> Dict[str, np.ndarray]:
+    """decomposable_attention with the scores formed from E4M3 codes: queries
+    quantized per (token, head), keys smoothed by mu and quantized per
+    (segment tile, head); the scores are scale * dq(q) . dq(k - mu) with the
+    products exact, V unquantized, and every LSE output shifted back by
+    scale * q . mu (the unquantized q)."""
+    qc, qs = quantize_queries(q)
+    q_dq = e4m3_decode(qc) * qs.T.astype(np.float64)[:, :, None]
+    r = decomposable_attention(q_dq, dequantized_keys(k_sink, mu), v_sink,
+                               dequantized_keys(k_cur, mu), v_cur,
+                               dequantized_keys(k_hist, mu), v_hist, scale)
+    if mu is not None:
+        nh, d = np.shape(q)[1], np.shape(q)[2]
+        m64 = np.asarray(mu, dtype=np.float64).reshape(nh, d)
+        shift = scale * np.einsum("qhd,hd->hq", np.asarray(q, dtype=np.float64), m64)
+        for key in ("lse_local", "lse_hist", "lse_full"):
+            r[key] = r[key] + shift
+    return r
