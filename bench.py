@@ -327,6 +327,75 @@ def session_measure(ispa, w: wl.Workload, n_stream: int = 3, seed: int = 2):
     return res
 
 
+def quantized_measure(ispa, w: wl.Workload, reps: int = 10, seed: int = 3):
+    """The E4M3 variants at the headline launch shape (the last warmup step:
+    O_local, O_full and D of one layer) and at one chunk's output projection,
+    each beside its bf16 counterpart, HIP events on the launch stream. The
+    E4M3 attention time includes the quantization of Q and K (the key mean is
+    timed on its own); the W8A8 projection time includes the per-token
+    quantization of X."""
+    dev, bf = "cuda", torch.bfloat16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    nh, d, h = w.n_heads, w.head_dim, w.hidden
+    n_hist = w.hist_per_step[-1]
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(*shape, device=dev, generator=gen) * std).to(bf)
+
+    q = rnd(w.n_q, nh, d, std=w.qkv_std)
+    kv = [rnd(n, nh, d, std=w.qkv_std) for n in (w.n_sink, w.n_sink, w.n_cur, w.n_cur,
+                                                 n_hist, n_hist)]
+    outs = [torch.empty(w.n_q, h, dtype=bf, device=dev) for _ in range(3)]
+    ws = torch.empty(ispa.ispa_attn_fp8_workspace_bytes(w.n_q, w.n_sink, w.n_cur, n_hist, nh, d),
+                     dtype=torch.uint8, device=dev)
+    mu = torch.empty(nh, d, dtype=bf, device=dev)
+    mws = torch.empty(ispa.ispa_key_mean_workspace_bytes(nh, d), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    o3 = dict(o_local=outs[0], o_full=outs[1], d_out=outs[2])
+    t_bf16 = timed(lambda: ispa.ispa_attn_decomp(q, *kv, w.sm_scale, **o3))
+    t_mean = timed(lambda: ispa.ispa_key_mean(kv[0], kv[2], kv[4], mu, mws))
+    t_fp8 = timed(lambda: ispa.ispa_attn_decomp_fp8(q, *kv, w.sm_scale, ws, k_mean=mu, **o3))
+    fl = attn_flops(w.n_q, w.n_sink + w.n_cur + n_hist, h)
+    del kv, ws
+    x = rnd(w.n_q, h, std=0.3)
+    wo = rnd(h, h, std=h ** -0.5)
+    y = torch.empty(w.n_q, h, dtype=bf, device=dev)
+    wq = torch.empty(h, h, dtype=torch.uint8, device=dev)
+    wsc = torch.empty(h, dtype=torch.float32, device=dev)
+    ispa.ispa_quantize_fp8(wo, wq, wsc)
+    pws = torch.empty(ispa.ispa_project_w8a8_workspace_bytes(w.n_q, h), dtype=torch.uint8,
+                      device=dev)
+    t_pb = timed(lambda: ispa.ispa_project(x, wo, y))
+    t_p8 = timed(lambda: ispa.ispa_project_w8a8(x, wq, wsc, y, pws))
+    pfl = 2.0 * w.n_q * h * h
+    return {
+        "attn_launch": f"n_q {w.n_q}, {w.n_sink} + {w.n_cur} local + {n_hist} history keys, "
+                       "O_local, O_full, D",
+        "attn_bf16_ms": round(t_bf16, 3),
+        "attn_fp8_ms": round(t_fp8, 3),
+        "attn_fp8_speedup": round(t_bf16 / t_fp8, 3),
+        "attn_fp8_tflops_bf16_equiv": round(fl / (t_fp8 * 1e-3) / 1e12, 1),
+        "key_mean_ms": round(t_mean, 3),
+        "proj_shape": [w.n_q, h, h],
+        "proj_bf16_us": round(t_pb * 1e3, 1),
+        "proj_w8a8_us": round(t_p8 * 1e3, 1),
+        "proj_w8a8_speedup": round(t_pb / t_p8, 3),
+        "proj_w8a8_tflops": round(pfl / (t_p8 * 1e-3) / 1e12, 1),
+    }
+
+
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -654,9 +723,12 @@ def main():
         "eps_gap_at_k": gap,
         "solve_info_nonzero": sum(1 for v in info if v != 0),
     }
+    del inp, ws, timing
+    torch.cuda.empty_cache()
+    print("[bench] E4M3 attention and W8A8 projection", file=sys.stderr, flush=True)
+    out["quantized"] = quantized_measure(ispa, w)
+    torch.cuda.empty_cache()
     if not a.no_stream:
-        del inp, ws, timing
-        torch.cuda.empty_cache()
         out["stream"] = stream_measure(ispa, w)
         torch.cuda.empty_cache()
         out["session"] = session_measure(ispa, w)

@@ -96,6 +96,57 @@ int ispa_attn_decomp(const void* q, int64_t n_q,
                      void* d_out, void* stream);
 
 /*
+ * Decomposable attention with E4M3 scores (§3.4 builds on FlashAttention-
+ * style LSE states and cites SageAttention's 8-bit attention; §4.4 runs
+ * ISPA with 8-bit quantization). Same arguments, outputs, split and merge
+ * as ispa_attn_decomp, with the scores formed from OCP E4M3 codes:
+ *   query row (token, head): scale s_q = absmax / 448, codes of q * (448 / absmax);
+ *   keys: smoothed as k - mu (fp32), then per head and per run of 64 keys
+ *     from each segment's start: s_k = absmax / 448, codes likewise;
+ *   score = sm_scale * s_q * s_k * sum_c dq(q_c) dq(k_c), products exact,
+ *     accumulated by the E4M3 matrix cores;
+ *   every LSE output gets sm_scale * (q . mu) added back (fp32, from the
+ *     bf16 q), so it estimates the unsmoothed LSE; the outputs O do not
+ *     depend on mu (a per-query constant shift of the scores).
+ * Codes round to nearest even; all-zero blocks get scale 0. V, P and P V
+ * are as in ispa_attn_decomp.
+ * k_mean           [n_heads, head_dim] bf16 smoothing vector mu, or NULL (mu = 0);
+ *                  e.g. from ispa_key_mean.
+ * head_dim         128 only (ISPA_ERR_UNSUPPORTED otherwise).
+ * workspace        ispa_attn_fp8_workspace_bytes(n_q, n_sink, n_cur, n_hist,
+ *                  n_heads, head_dim) bytes, 16-byte aligned: the codes and
+ *                  scales (1 byte per Q/K element plus 4 bytes per scale).
+ * Errors: those of ispa_attn_decomp, plus ISPA_ERR_WORKSPACE.
+ */
+size_t ispa_attn_fp8_workspace_bytes(int64_t n_q, int64_t n_sink, int64_t n_cur,
+                                     int64_t n_hist, int n_heads, int head_dim);
+int ispa_attn_decomp_fp8(const void* q, int64_t n_q,
+                         const void* k_sink, const void* v_sink, int64_t n_sink,
+                         const void* k_cur, const void* v_cur, int64_t n_cur,
+                         const void* k_hist, const void* v_hist, int64_t n_hist,
+                         int n_heads, int head_dim, float sm_scale,
+                         const void* k_mean,
+                         void* o_local, float* lse_local,
+                         void* o_hist, float* lse_hist,
+                         void* o_full, float* lse_full,
+                         void* d_out, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Mean key of the given segments, per head and channel (the smoothing
+ * vector of ispa_attn_decomp_fp8): mu [n_heads, head_dim] bf16 = the fp32
+ * column sums over all n_sink + n_cur + n_hist keys (in a fixed order, so
+ * the result is deterministic), divided by the count, rounded to bf16.
+ * head_dim 128 only. workspace: ispa_key_mean_workspace_bytes(n_heads,
+ * head_dim) bytes. Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (no keys),
+ * ISPA_ERR_UNSUPPORTED, ISPA_ERR_WORKSPACE, ISPA_ERR_ALIGN.
+ */
+size_t ispa_key_mean_workspace_bytes(int n_heads, int head_dim);
+int ispa_key_mean(const void* k_sink, int64_t n_sink, const void* k_cur, int64_t n_cur,
+                  const void* k_hist, int64_t n_hist, int n_heads, int head_dim,
+                  void* mu, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Warmup statistics (§3.1 item 2: the accumulated dual-stream activations).
  *
  * For each of n_batch independent problems b (e.g. layers):

@@ -42,6 +42,15 @@ lib.ispa_version.argtypes = []
 lib.ispa_attn_decomp.restype = _i
 lib.ispa_attn_decomp.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p, _i64, _i, _i, _f,
                                  _p, _p, _p, _p, _p, _p, _p, _p]
+lib.ispa_attn_fp8_workspace_bytes.restype = _sz
+lib.ispa_attn_fp8_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i, _i]
+lib.ispa_attn_decomp_fp8.restype = _i
+lib.ispa_attn_decomp_fp8.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p, _i64, _i, _i,
+                                     _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+lib.ispa_key_mean_workspace_bytes.restype = _sz
+lib.ispa_key_mean_workspace_bytes.argtypes = [_i, _i]
+lib.ispa_key_mean.restype = _i
+lib.ispa_key_mean.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i, _i, _p, _p, _sz, _p]
 lib.ispa_gram_accumulate.restype = _i
 lib.ispa_gram_accumulate.argtypes = [_p, _p, _i64, _i, _i, _p, _p, _p, _i, _p]
 lib.ispa_ridge_workspace_bytes.restype = _sz
@@ -147,7 +156,9 @@ EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram
             "ispa_drift_prepare", "ispa_drift_score", "ispa_session_workspace_bytes",
             "ispa_session_create", "ispa_session_destroy", "ispa_session_cache",
             "ispa_session_layer", "ispa_session_end_chunk", "ispa_session_query",
-            "ispa_quantize_fp8", "ispa_project_w8a8_workspace_bytes", "ispa_project_w8a8")
+            "ispa_quantize_fp8", "ispa_project_w8a8_workspace_bytes", "ispa_project_w8a8",
+            "ispa_attn_fp8_workspace_bytes", "ispa_attn_decomp_fp8",
+            "ispa_key_mean_workspace_bytes", "ispa_key_mean")
 
 
 class IspaError(RuntimeError):
@@ -187,13 +198,9 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "") -> int:
     return t.data_ptr()
 
 
-def ispa_attn_decomp(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: float, *,
-                     o_local=None, lse_local=None, o_hist=None, lse_hist=None, o_full=None,
-                     lse_full=None, d_out=None, stream=None) -> None:
-    """q [n_q, H, d]; k_*/v_* [n, H, d] bf16 (k_hist/v_hist may have n = 0).
-    Outputs are preallocated tensors: o_* / d_out [n_q, H*d] bf16, lse_*
-    [H, n_q] fp32; pass the ones to produce."""
-    bf, f32 = torch.bfloat16, torch.float32
+def _attn_args(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, outs):
+    bf = torch.bfloat16
+    o_local, lse_local, o_hist, lse_hist, o_full, lse_full, d_out = outs
     n_q, n_heads, head_dim = q.shape
     segs = []
     for name, k, v in (("sink", k_sink, v_sink), ("cur", k_cur, v_cur), ("hist", k_hist, v_hist)):
@@ -208,13 +215,77 @@ def ispa_attn_decomp(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: 
     for name, t in (("lse_local", lse_local), ("lse_hist", lse_hist), ("lse_full", lse_full)):
         if t is not None and tuple(t.shape) != (n_heads, n_q):
             raise ValueError(f"{name}: expected shape {(n_heads, n_q)}")
-    st = lib.ispa_attn_decomp(
-        _ptr(q, bf, "q"), n_q, *segs, n_heads, head_dim, float(sm_scale),
-        _ptr(o_local, bf, "o_local"), _ptr(lse_local, f32, "lse_local"),
-        _ptr(o_hist, bf, "o_hist"), _ptr(lse_hist, f32, "lse_hist"),
-        _ptr(o_full, bf, "o_full"), _ptr(lse_full, f32, "lse_full"),
-        _ptr(d_out, bf, "d_out"), _stream(stream))
+    f32 = torch.float32
+    out_ptrs = [_ptr(o_local, bf, "o_local"), _ptr(lse_local, f32, "lse_local"),
+                _ptr(o_hist, bf, "o_hist"), _ptr(lse_hist, f32, "lse_hist"),
+                _ptr(o_full, bf, "o_full"), _ptr(lse_full, f32, "lse_full"),
+                _ptr(d_out, bf, "d_out")]
+    return n_q, n_heads, head_dim, segs, out_ptrs
+
+
+def ispa_attn_decomp(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: float, *,
+                     o_local=None, lse_local=None, o_hist=None, lse_hist=None, o_full=None,
+                     lse_full=None, d_out=None, stream=None) -> None:
+    """q [n_q, H, d]; k_*/v_* [n, H, d] bf16 (k_hist/v_hist may have n = 0).
+    Outputs are preallocated tensors: o_* / d_out [n_q, H*d] bf16, lse_*
+    [H, n_q] fp32; pass the ones to produce."""
+    n_q, n_heads, head_dim, segs, outs = _attn_args(
+        q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist,
+        (o_local, lse_local, o_hist, lse_hist, o_full, lse_full, d_out))
+    st = lib.ispa_attn_decomp(_ptr(q, torch.bfloat16, "q"), n_q, *segs, n_heads, head_dim,
+                              float(sm_scale), *outs, _stream(stream))
     _check("ispa_attn_decomp", st)
+
+
+def ispa_attn_fp8_workspace_bytes(n_q: int, n_sink: int, n_cur: int, n_hist: int,
+                                  n_heads: int, head_dim: int) -> int:
+    return int(lib.ispa_attn_fp8_workspace_bytes(n_q, n_sink, n_cur, n_hist, n_heads, head_dim))
+
+
+def ispa_attn_decomp_fp8(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: float,
+                         workspace, *, k_mean=None, o_local=None, lse_local=None, o_hist=None,
+                         lse_hist=None, o_full=None, lse_full=None, d_out=None,
+                         stream=None) -> None:
+    """ispa_attn_decomp with E4M3 scores; k_mean [H, d] bf16 (or None) is the
+    smoothing vector, workspace a uint8 tensor of
+    ispa_attn_fp8_workspace_bytes(...) bytes."""
+    n_q, n_heads, head_dim, segs, outs = _attn_args(
+        q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist,
+        (o_local, lse_local, o_hist, lse_hist, o_full, lse_full, d_out))
+    if k_mean is not None and tuple(k_mean.shape) != (n_heads, head_dim):
+        raise ValueError("k_mean: expected shape (n_heads, head_dim)")
+    st = lib.ispa_attn_decomp_fp8(
+        _ptr(q, torch.bfloat16, "q"), n_q, *segs, n_heads, head_dim, float(sm_scale),
+        _ptr(k_mean, torch.bfloat16, "k_mean"), *outs, _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ispa_attn_decomp_fp8", st)
+
+
+def ispa_key_mean_workspace_bytes(n_heads: int, head_dim: int) -> int:
+    return int(lib.ispa_key_mean_workspace_bytes(n_heads, head_dim))
+
+
+def ispa_key_mean(k_sink, k_cur, k_hist, mu, workspace, *, stream=None) -> None:
+    """mu [H, d] bf16 = mean of the keys of the given segments ([n, H, d] bf16,
+    any may be None)."""
+    segs = []
+    shape = None
+    for name, k in (("k_sink", k_sink), ("k_cur", k_cur), ("k_hist", k_hist)):
+        n = 0 if k is None else k.shape[0]
+        if k is not None:
+            if shape is not None and k.shape[1:] != shape:
+                raise ValueError("ispa_key_mean: segment shapes differ")
+            shape = k.shape[1:]
+        segs += [_ptr(k, torch.bfloat16, name) if n else 0, n]
+    if shape is None:
+        raise ValueError("ispa_key_mean: no keys")
+    n_heads, head_dim = shape
+    if tuple(mu.shape) != (n_heads, head_dim):
+        raise ValueError("mu: expected shape (n_heads, head_dim)")
+    st = lib.ispa_key_mean(*segs, n_heads, head_dim, _ptr(mu, torch.bfloat16, "mu"),
+                           _ptr(workspace, None, "workspace"),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ispa_key_mean", st)
 
 
 def ispa_gram_accumulate(x, d, G, C, E=None, *, zero_first: bool = False, stream=None) -> None:

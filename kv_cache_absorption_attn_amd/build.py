@@ -25,7 +25,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libispa.so")
 
 SOURCES = ["attn_decomp.hip", "gram.hip", "gemm_f32.hip", "solve.hip", "ispa_api.hip",
-           "kv_cache.hip", "session.hip", "nt_gemm.hip", "w8a8.hip"]
+           "kv_cache.hip", "session.hip", "nt_gemm.hip", "w8a8.hip",
+           "attn_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

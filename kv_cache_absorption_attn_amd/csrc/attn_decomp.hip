@@ -34,6 +34,16 @@
 // The running max is only moved when the tile max exceeds it by more than
 // 2^8 (the result is exact either way; it only bounds p <= 256), which keeps
 // the O rescale off the common path.
+//
+// E4M3 instance (head_dim 128): the scores come from 8-bit codes, the
+// SageAttention-style quantized attention the paper's §3.4 cites. Queries
+// carry one scale per (token, head), the smoothed keys one per (64-key tile,
+// head); K Q^T runs as 8 MFMA 32x32x64 per tile on the codes (a K tile is
+// 8 KB: 128-byte rows, staged and swizzled like a 64-wide bf16 tile) and
+// the product of the two scales joins the softmax scale in the one FMA per
+// score that forms the exponent, so the softmax costs what it costs on bf16.
+// V, P and P V are unchanged; the LSE outputs get the smoothing shift
+// scale * q . mu added back.
 
 #include <type_traits>
 
@@ -58,10 +68,33 @@ template <int D>
 __device__ __forceinline__ int swz(int r) { return lds_swz<D>(r); }
 
 struct Seg {
-  const uint16_t* k;
+  const uint16_t* k;     // bf16 keys, or the E4M3 codes viewed as 16-bit pairs
   const uint16_t* v;
   int64_t n;
+  const float* ksc;      // E4M3: scales [tiles][n_heads]
 };
+
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
+
+// E4M3 K operand of a 64-key tile with 128-byte rows (a tile of 64-wide
+// 16-bit rows, swizzled by lds_swz<64>): key row r, k-step t (64 channels),
+// lane half h: channels 64 t + 32 h .. + 31, the logical 16-byte chunks
+// 4 t + 2 h and 4 t + 2 h + 1.
+__device__ __forceinline__ v8i32 k8_frag(const uint16_t* ks, int r, int t, int h) {
+  const int sw = lds_swz<64>(r);
+  const uint16_t* row = ks + r * 64;
+  const v4i32_t lo = *reinterpret_cast<const v4i32_t*>(row + 8 * ((4 * t + 2 * h) ^ sw));
+  const v4i32_t hi = *reinterpret_cast<const v4i32_t*>(row + 8 * ((4 * t + 2 * h + 1) ^ sw));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// 32x32x64 E4M3 MFMA (both operands E4M3, no block scales): lane l holds the
+// 32 consecutive k of row (A) / column (B) l % 32 from k = 32 (l / 32); the
+// result layout is that of mfma32x32x16.
+__device__ __forceinline__ f32x16 mfma_e4m3(v8i32 a, v8i32 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 
 // Direct-to-LDS loads of one 64-key tile of K and V. Each lane's byte offset
 // inside a full tile is fixed, so a full tile only moves a uniform base.
@@ -168,17 +201,21 @@ __device__ __forceinline__ void load_o(const uint16_t* in, f32x16* o, int64_t qi
   }
 }
 
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnParams p) {
-  constexpr int TBUF = kKTile * D;   // one K or V tile (elements)
+  static_assert(!F8 || D == 128, "the E4M3 instance is built for head_dim 128");
+  constexpr int TBUF = kKTile * D;   // one V tile (elements)
+  constexpr int KD = F8 ? D / 2 : D; // K tile row in 16-bit units
+  constexpr int TBUFK = kKTile * KD; // one K tile
   constexpr int NB = D / 32;         // 32-wide d blocks of O^T
-  constexpr int NT = D / 16;         // k-steps of K Q^T
+  constexpr int NT = F8 ? D / 64 : D / 16;  // k-steps of K Q^T
+  using KF = std::conditional_t<F8, v8i32, bf16x8>;  // K operand of one MFMA
   constexpr int PSLOT = kPairs * 2 * 4 * 64;  // P^T operands of one tile (16-byte units)
   // K and V tiles, two buffers each, and the P^T hand-off, two slots: every
   // access names a fixed array, so the compiler can see that a load into one
   // buffer never aliases the reads of another and needs no early wait.
-  __shared__ __attribute__((aligned(16))) uint16_t sk0[TBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sk1[TBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[TBUFK];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[TBUFK];
   __shared__ __attribute__((aligned(16))) uint16_t sv0[TBUF];
   __shared__ __attribute__((aligned(16))) uint16_t sv1[TBUF];
   __shared__ uint4 sp0[PSLOT];                 // [pair][qb][st][lane]
@@ -219,13 +256,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
     sg.k = s0 ? p.k[0] : (s1 ? p.k[1] : p.k[2]);
     sg.v = s0 ? p.v[0] : (s1 ? p.v[1] : p.v[2]);
     sg.n = s0 ? p.n[0] : (s1 ? p.n[1] : p.n[2]);
+    if constexpr (F8) {
+      sg.k = reinterpret_cast<const uint16_t*>(s0 ? p.k8[0] : (s1 ? p.k8[1] : p.k8[2]));
+      sg.ksc = s0 ? p.ksc[0] : (s1 ? p.ksc[1] : p.ksc[2]);
+    }
     row0 = static_cast<int64_t>(t) * kKTile;
     const int64_t rem = sg.n - row0;
     valid = rem < kKTile ? static_cast<int>(rem) : kKTile;
   };
 
-  TileLoader<D, kPairs> loader;
+  TileLoader<D, kPairs> loader;  // V, and K of the bf16 instance
   loader.init(rs, head, __builtin_amdgcn_readfirstlane(pair), lane);
+  TileLoader<KD, kPairs> loader8;  // K codes of the E4M3 instance (rows of D bytes)
+  if constexpr (F8) loader8.init(rs / 2, head, __builtin_amdgcn_readfirstlane(pair), lane);
+  auto issue_k = [&](const Seg& sg, int64_t row0, int valid, uint16_t* dst) {
+    if constexpr (F8)
+      loader8.issue_k(sg, row0, valid, rs / 2, dst);
+    else
+      loader.issue_k(sg, row0, valid, rs, dst);
+  };
   const int prow = pair * 64;  // this pair's entries in the per-query arrays
   const int prow2 = pair * 128;  // and in the per-lane rescale factors
 
@@ -236,14 +285,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
     // runs one tile ahead of its own softmax: while the vector ALU works on
     // the scores of tile j, the matrix cores compute those of tile j+1, one
     // MFMA between consecutive slices of the softmax.
-    bf16x8 qf[2][NT];
+    bf16x8 qf[2][F8 ? 1 : NT];
+    v8i32 qf8[2][F8 ? NT : 1];
+    // E4M3: scale_log2 x the query's scale (times a tile's key scale, the
+    // multiplier of the raw code products), and the smoothing shift of the LSE
+    float qsl[2] = {p.scale_log2, p.scale_log2}, lcorr[2] = {0.f, 0.f};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb) {
+      if constexpr (F8) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        qf[qb][t] = qvalid[qb] ? *reinterpret_cast<const bf16x8*>(p.q + static_cast<int64_t>(qi[qb]) * rs + head * D +
-                                                                  16 * t + 8 * hf)
-                               : bf16x8{};
+        for (int t = 0; t < NT; ++t)
+          qf8[qb][t] = qvalid[qb] ? *reinterpret_cast<const v8i32*>(
+                                        p.q8 + static_cast<int64_t>(qi[qb]) * rs + head * D +
+                                        64 * t + 32 * hf)
+                                  : v8i32{};
+        qsl[qb] = qvalid[qb] ? p.scale_log2 * p.qsc[static_cast<int64_t>(head) * p.n_q + qi[qb]]
+                             : 0.f;
+        if (p.qmu && qvalid[qb]) lcorr[qb] = p.qmu[static_cast<int64_t>(head) * p.n_q + qi[qb]];
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          qf[qb][t] = qvalid[qb] ? *reinterpret_cast<const bf16x8*>(
+                                       p.q + static_cast<int64_t>(qi[qb]) * rs + head * D +
+                                       16 * t + 8 * hf)
+                                 : bf16x8{};
+      }
+    }
+    // LSE output (natural log) of a log2-unit value
+    auto lse_out = [&](float v2, int qb) {
+      if constexpr (F8)
+        return v2 * kLn2 + lcorr[qb];
+      else
+        return v2 * kLn2;
+    };
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
     float lse_loc2[2] = {-INFINITY, -INFINITY};
     {
@@ -251,10 +325,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
       int valid;
       int64_t row0;
       tile_of(0, sg, row0, valid);
-      loader.issue_k(sg, row0, valid, rs, sk0);
+      issue_k(sg, row0, valid, sk0);
       if (T > 1) {
         tile_of(1, sg, row0, valid);
-        loader.issue_k(sg, row0, valid, rs, sk1);
+        issue_k(sg, row0, valid, sk1);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -262,7 +336,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
 
     // S^T[key half][query block] of the even (sa) and odd (sb) tiles
     f32x16 sa[2][2], sb[2][2];
-    {
+    if constexpr (F8) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const v8i32 a0 = k8_frag(sk0, l32, t, hf), a1 = k8_frag(sk0, 32 + l32, t, hf);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sa[0][qb] = mfma_e4m3(a0, qf8[qb][t], t ? sa[0][qb] : f32x16{});
+          sa[1][qb] = mfma_e4m3(a1, qf8[qb][t], t ? sa[1][qb] : f32x16{});
+        }
+      }
+    } else {
       bf16x8 a0 = k_frag<D>(sk0, l32, hf), a1 = k_frag<D>(sk0, 32 + l32, hf);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -294,7 +378,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
     // their exponentials are dropped, in a separate instance of this code.
     auto body = [&](auto tail_c, auto qk_c, f32x16(&sc)[2][2], f32x16(&sn)[2][2],
                     const uint16_t* __restrict__ ks, uint4* __restrict__ sp,
-                    float* __restrict__ sal, int valid) __attribute__((always_inline)) {
+                    float* __restrict__ sal, int valid, const float(&cq)[2])
+        __attribute__((always_inline)) {
       constexpr bool TAIL = decltype(tail_c)::value;
       constexpr bool QK = decltype(qk_c)::value;
       constexpr int NMF = 4 * NT;           // MFMAs of one tile's K Q^T
@@ -314,12 +399,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
       const int kf = r32 * D + 8 * (h2 ^ (swz<D>(r32) & 1));
       const int kx = 16 * (swz<D>(r32) >> 1);
       auto kfrag = [&](int t, int half) {
-        return *reinterpret_cast<const bf16x8*>(ks + kf + 32 * D * half + (kx ^ (16 * t)));
+        if constexpr (F8)
+          return k8_frag(ks, r32 + 32 * half, t, h2);
+        else
+          return *reinterpret_cast<const bf16x8*>(ks + kf + 32 * D * half + (kx ^ (16 * t)));
       };
       // operands of the two key halves, each read at the top of the slot two
       // slots before its first MFMA (the register being reloaded was last
       // read by the previous slot's MFMA)
-      bf16x8 f0, f1;
+      KF f0, f1;
       if constexpr (QK) {
         f0 = kfrag(0, 0);
         f1 = kfrag(0, 1);
@@ -357,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
           for (int qb = 0; qb < 2; ++qb) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[qb]),
                                                              __float_as_uint(mx[qb]), false, false);
-            const float mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+            const float mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cq[qb];
             const bool need = mt > m_run[qb] + kRescaleThreshold;
             const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
             m_run[qb] = need ? mt : m_run[qb];
@@ -374,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
 #pragma unroll
           for (int i = 4 * h; i < 4 * h + 4; ++i) {
             float e = __builtin_amdgcn_exp2f(
-                fmaf(sc[st / 2][qb][8 * (st % 2) + i], p.scale_log2, -m_run[qb]));
+                fmaf(sc[st / 2][qb][8 * (st % 2) + i], cq[qb], -m_run[qb]));
             if constexpr (TAIL) {
               const int key = 32 * (st / 2) + 8 * ((8 * (st % 2) + i) / 4) + 4 * h2 + (i % 4);
               if (key >= valid) e = 0.f;
@@ -390,7 +478,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
         }
         if constexpr (QK) {
           const int t = u / 4, kh = (u / 2) % 2, qb = u % 2;
-          sn[kh][qb] = mfma32x32x16(kh ? f1 : f0, qf[qb][t], t ? sn[kh][qb] : f32x16{});
+          if constexpr (F8)
+            sn[kh][qb] = mfma_e4m3(kh ? f1 : f0, qf8[qb][t], t ? sn[kh][qb] : f32x16{});
+          else
+            sn[kh][qb] = mfma32x32x16(kh ? f1 : f0, qf[qb][t], t ? sn[kh][qb] : f32x16{});
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -414,11 +505,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
         int valid;
         int64_t row0;
         tile_of(it, sg, row0, valid);
+        float cq[2] = {p.scale_log2, p.scale_log2};
+        if constexpr (F8) {
+          const float sk = sg.ksc[(row0 / kKTile) * p.n_heads + head];
+          cq[0] = qsl[0] * sk;
+          cq[1] = qsl[1] * sk;
+        }
         auto run = [&](auto tail_c, auto qk_c) __attribute__((always_inline)) {
           if constexpr (BUF == 0)
-            body(tail_c, qk_c, sa, sb, ks, sp, sal, valid);
+            body(tail_c, qk_c, sa, sb, ks, sp, sal, valid, cq);
           else
-            body(tail_c, qk_c, sb, sa, ks, sp, sal, valid);
+            body(tail_c, qk_c, sb, sa, ks, sp, sal, valid, cq);
         };
         if (it + 1 < T) {
           if (valid == kKTile)
@@ -439,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
             lse_loc2[qb] = m_run[qb] + __builtin_amdgcn_logf(lt);
             if (hf == 0) s_inv_loc[prow + 32 * qb + l32] = 1.f / lt;
             if (qvalid[qb] && p.lse_local && hf == 0)
-              p.lse_local[head * p.n_q + qi[qb]] = lse_loc2[qb] * kLn2;
+              p.lse_local[head * p.n_q + qi[qb]] = lse_out(lse_loc2[qb], qb);
             m_run[qb] = -INFINITY;
             l_run[qb] = 0.f;
           }
@@ -471,9 +568,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
             s_wh[prow + 32 * qb + l32] = w_h;
             if (qvalid[qb]) {
               if (split && p.need_hist && p.lse_hist)
-                p.lse_hist[head * p.n_q + qi[qb]] = lse2 * kLn2;
+                p.lse_hist[head * p.n_q + qi[qb]] = lse_out(lse2, qb);
               if ((!split || p.need_hist) && p.lse_full)
-                p.lse_full[head * p.n_q + qi[qb]] = lse_f2 * kLn2;
+                p.lse_full[head * p.n_q + qi[qb]] = lse_out(lse_f2, qb);
             }
           }
         }
@@ -523,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
       loader.issue_v(sg, row0, valid, rs, nvs);
       if (it + 2 < T) {
         tile_of(it + 2, sg, row0, valid);
-        loader.issue_k(sg, row0, valid, rs, nks);
+        issue_k(sg, row0, valid, nks);
       }
     }
     if (it >= 1) {
@@ -623,10 +720,17 @@ hipError_t launch_attn_decomp(AttnParams p, int head_dim, hipStream_t stream) {
   p.n_qtiles = static_cast<int>((p.n_q + kQTile - 1) / kQTile);
   const int blocks = p.n_qtiles * p.n_heads;
   if (blocks == 0) return hipSuccess;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attn_decomp_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_decomp_kernel<64>, dim3(blocks), dim3(kThreads), 0, stream, p);
+  if (p.q8) {
+    if (head_dim != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_decomp_kernel<128, true>), dim3(blocks), dim3(kThreads), 0, stream,
+                       p);
+  } else if (head_dim == 128) {
+    hipLaunchKernelGGL((attn_decomp_kernel<128, false>), dim3(blocks), dim3(kThreads), 0, stream,
+                       p);
+  } else {
+    hipLaunchKernelGGL((attn_decomp_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, stream,
+                       p);
+  }
   return hipGetLastError();
 }
 

@@ -180,11 +180,19 @@ const char* ispa_status_string(int status) {
 
 int ispa_version(void) { return 100; }
 
-int ispa_attn_decomp(const void* q, int64_t n_q, const void* k_sink, const void* v_sink,
-                     int64_t n_sink, const void* k_cur, const void* v_cur, int64_t n_cur,
-                     const void* k_hist, const void* v_hist, int64_t n_hist, int n_heads,
-                     int head_dim, float sm_scale, void* o_local, float* lse_local, void* o_hist,
-                     float* lse_hist, void* o_full, float* lse_full, void* d_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and parameters shared by the bf16 and E4M3 attention entry
+// points. Returns ISPA_OK with *run = false when there is nothing to do.
+int attn_setup(const void* q, int64_t n_q, const void* k_sink, const void* v_sink,
+               int64_t n_sink, const void* k_cur, const void* v_cur, int64_t n_cur,
+               const void* k_hist, const void* v_hist, int64_t n_hist, int n_heads,
+               int head_dim, float sm_scale, void* o_local, float* lse_local, void* o_hist,
+               float* lse_hist, void* o_full, float* lse_full, void* d_out,
+               ispa::AttnParams* out, bool* run) {
+  *run = false;
   if (n_q < 0 || n_sink < 0 || n_cur < 0 || n_hist < 0 || n_heads < 1) return ISPA_ERR_SHAPE;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return ISPA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return ISPA_ERR_UNSUPPORTED;
@@ -227,7 +235,133 @@ int ispa_attn_decomp(const void* q, int64_t n_q, const void* k_sink, const void*
   const bool only_full = !o_local && !lse_local && !o_hist && !lse_hist && !d_out;
   p.mode = only_full ? 1 : 0;
   p.need_hist = (o_hist || lse_hist || o_full || lse_full || d_out) ? 1 : 0;
+  *out = p;
+  *run = true;
+  return ISPA_OK;
+}
+
+// Workspace of the E4M3 attention: query codes, scales and shifts, then per
+// segment the key codes and tile scales.
+struct AttnFp8Ws {
+  uint8_t* q8;
+  float* qsc;
+  float* qmu;
+  uint8_t* k8[3];
+  float* ksc[3];
+  size_t bytes;
+};
+
+AttnFp8Ws attn_fp8_layout(void* base, int64_t n_q, const int64_t n[3], int n_heads) {
+  AttnFp8Ws w{};
+  const size_t row = static_cast<size_t>(n_heads) * 128;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  w.q8 = reinterpret_cast<uint8_t*>(p + off);  off = align_up(off + n_q * row);
+  w.qsc = reinterpret_cast<float*>(p + off);   off = align_up(off + n_q * n_heads * 4);
+  w.qmu = reinterpret_cast<float*>(p + off);   off = align_up(off + n_q * n_heads * 4);
+  for (int g = 0; g < 3; ++g) {
+    w.k8[g] = reinterpret_cast<uint8_t*>(p + off);
+    off = align_up(off + n[g] * row);
+    w.ksc[g] = reinterpret_cast<float*>(p + off);
+    off = align_up(off + ispa::key_tiles(n[g]) * n_heads * 4);
+  }
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ispa_attn_decomp(const void* q, int64_t n_q, const void* k_sink, const void* v_sink,
+                     int64_t n_sink, const void* k_cur, const void* v_cur, int64_t n_cur,
+                     const void* k_hist, const void* v_hist, int64_t n_hist, int n_heads,
+                     int head_dim, float sm_scale, void* o_local, float* lse_local, void* o_hist,
+                     float* lse_hist, void* o_full, float* lse_full, void* d_out, void* stream) {
+  ispa::AttnParams p{};
+  bool run = false;
+  const int st = attn_setup(q, n_q, k_sink, v_sink, n_sink, k_cur, v_cur, n_cur, k_hist, v_hist,
+                            n_hist, n_heads, head_dim, sm_scale, o_local, lse_local, o_hist,
+                            lse_hist, o_full, lse_full, d_out, &p, &run);
+  if (st != ISPA_OK || !run) return st;
   return hip_status(ispa::launch_attn_decomp(p, head_dim, as_stream(stream)));
+}
+
+size_t ispa_attn_fp8_workspace_bytes(int64_t n_q, int64_t n_sink, int64_t n_cur, int64_t n_hist,
+                                     int n_heads, int head_dim) {
+  if (n_q < 0 || n_sink < 0 || n_cur < 0 || n_hist < 0 || n_heads < 1 || head_dim != 128)
+    return 0;
+  const int64_t n[3] = {n_sink, n_cur, n_hist};
+  return attn_fp8_layout(nullptr, n_q, n, n_heads).bytes;
+}
+
+int ispa_attn_decomp_fp8(const void* q, int64_t n_q, const void* k_sink, const void* v_sink,
+                         int64_t n_sink, const void* k_cur, const void* v_cur, int64_t n_cur,
+                         const void* k_hist, const void* v_hist, int64_t n_hist, int n_heads,
+                         int head_dim, float sm_scale, const void* k_mean, void* o_local,
+                         float* lse_local, void* o_hist, float* lse_hist, void* o_full,
+                         float* lse_full, void* d_out, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  ispa::AttnParams p{};
+  bool run = false;
+  const int st = attn_setup(q, n_q, k_sink, v_sink, n_sink, k_cur, v_cur, n_cur, k_hist, v_hist,
+                            n_hist, n_heads, head_dim, sm_scale, o_local, lse_local, o_hist,
+                            lse_hist, o_full, lse_full, d_out, &p, &run);
+  if (st != ISPA_OK) return st;
+  if (head_dim != 128) return ISPA_ERR_UNSUPPORTED;
+  if (k_mean && !aligned16(k_mean)) return ISPA_ERR_ALIGN;
+  if (!run) return ISPA_OK;
+  if (!workspace ||
+      ws_bytes < ispa_attn_fp8_workspace_bytes(n_q, n_sink, n_cur, n_hist, n_heads, head_dim))
+    return ISPA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ISPA_ERR_ALIGN;
+  const int64_t n[3] = {n_sink, n_cur, n_hist};
+  const AttnFp8Ws w = attn_fp8_layout(workspace, n_q, n, n_heads);
+  const hipStream_t s = as_stream(stream);
+  const uint16_t* mu = static_cast<const uint16_t*>(k_mean);
+  ISPA_TRY(ispa::launch_quantize_queries_fp8(p.q, n_q, n_heads, mu, sm_scale, w.q8, w.qsc,
+                                             mu ? w.qmu : nullptr, s));
+  for (int g = 0; g < 3; ++g)
+    ISPA_TRY(ispa::launch_quantize_key_tiles_fp8(p.k[g], n[g], n_heads, mu, w.k8[g], w.ksc[g],
+                                                 s));
+  p.q8 = w.q8;
+  p.qsc = w.qsc;
+  p.qmu = mu ? w.qmu : nullptr;
+  for (int g = 0; g < 3; ++g) {
+    p.k8[g] = w.k8[g];
+    p.ksc[g] = w.ksc[g];
+  }
+  return hip_status(ispa::launch_attn_decomp(p, head_dim, s));
+}
+
+size_t ispa_key_mean_workspace_bytes(int n_heads, int head_dim) {
+  if (n_heads < 1 || head_dim != 128) return 0;
+  return static_cast<size_t>(ispa::key_mean_splits()) * n_heads * head_dim * sizeof(float);
+}
+
+int ispa_key_mean(const void* k_sink, int64_t n_sink, const void* k_cur, int64_t n_cur,
+                  const void* k_hist, int64_t n_hist, int n_heads, int head_dim, void* mu,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  if (!mu) return ISPA_ERR_NULL;
+  if (n_sink < 0 || n_cur < 0 || n_hist < 0 || n_heads < 1) return ISPA_ERR_SHAPE;
+  if ((n_sink > 0 && !k_sink) || (n_cur > 0 && !k_cur) || (n_hist > 0 && !k_hist))
+    return ISPA_ERR_NULL;
+  if (n_sink + n_cur + n_hist < 1) return ISPA_ERR_SHAPE;
+  if (head_dim != 128) return ISPA_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < ispa_key_mean_workspace_bytes(n_heads, head_dim))
+    return ISPA_ERR_WORKSPACE;
+  const void* ptrs[] = {k_sink, k_cur, k_hist, mu, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return ISPA_ERR_ALIGN;
+  ispa::KeySegs segs{};
+  segs.k[0] = static_cast<const uint16_t*>(k_sink);
+  segs.k[1] = static_cast<const uint16_t*>(k_cur);
+  segs.k[2] = static_cast<const uint16_t*>(k_hist);
+  segs.n[0] = n_sink;
+  segs.n[1] = n_cur;
+  segs.n[2] = n_hist;
+  return hip_status(ispa::launch_key_mean(segs, n_heads, static_cast<float*>(workspace),
+                                          static_cast<uint16_t*>(mu), as_stream(stream)));
 }
 
 int ispa_gram_accumulate(const void* x, const void* d, int64_t n_tok, int h, int n_batch,

@@ -25,9 +25,34 @@ struct AttnParams {
   int n_qtiles;
   int mode;                  // 0: local / history split + merge; 1: one pass (full only)
   int need_hist;             // split mode: history phase and merge needed
+  // E4M3 scores (head_dim 128; used when q8 is set): query codes [n_q,
+  // n_heads, D] with scales [n_heads, n_q]; per segment the smoothed key
+  // codes [n_s, n_heads, D] with scales [tiles_s, n_heads] (64-key tiles);
+  // qmu [n_heads, n_q]: scale * q . mu added to every LSE output (or null)
+  const uint8_t* q8;
+  const float* qsc;
+  const uint8_t* k8[3];
+  const float* ksc[3];
+  const float* qmu;
 };
 // Fills p.n_qtiles, then launches.
 hipError_t launch_attn_decomp(AttnParams p, int head_dim, hipStream_t stream);
+
+// E4M3 attention operands (head_dim 128).
+struct KeySegs {
+  const uint16_t* k[3];      // [n_s, n_heads, 128] bf16
+  int64_t n[3];
+};
+hipError_t launch_quantize_queries_fp8(const uint16_t* q, int64_t n_q, int n_heads,
+                                       const uint16_t* mu, float sm_scale, uint8_t* q8,
+                                       float* qsc, float* qmu, hipStream_t stream);
+int64_t key_tiles(int64_t n);  // 64-key tiles of a segment
+hipError_t launch_quantize_key_tiles_fp8(const uint16_t* k, int64_t n, int n_heads,
+                                         const uint16_t* mu, uint8_t* k8, float* ksc,
+                                         hipStream_t stream);
+int key_mean_splits();         // partial sums of the key mean (rows of its workspace)
+hipError_t launch_key_mean(const KeySegs& segs, int n_heads, float* part, uint16_t* mu,
+                           hipStream_t stream);
 int attn_q_tile_min();  // smallest query tile of any attention kernel
 
 // ---------------------------------------------------------------- Gram

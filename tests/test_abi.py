@@ -116,6 +116,46 @@ def test_score_apply_project_validation():
     assert p(A, A, A, 0, 128, 128, 0) == OK
 
 
+def test_fp8_attention_validation():
+    """Argument checks of the E4M3 attention and the key mean that return
+    before any launch."""
+    wsb = ispa.ispa_attn_fp8_workspace_bytes
+    need = wsb(100, 10, 20, 30, 2, 128)
+    assert need >= 160 * 256 + 100 * 2 * 8
+    assert wsb(100, 10, 20, 30, 2, 64) == 0 and wsb(-1, 0, 1, 0, 2, 128) == 0
+    f = _lib.lib.ispa_attn_decomp_fp8
+    base = [A, 100, A, A, 10, A, A, 20, A, A, 30, 2, 128, 0.1, 0, A, 0, 0, 0, A, 0, 0, A, need, 0]
+
+    def call(**kw):
+        names = ["q", "n_q", "ks", "vs", "n_sink", "kc", "vc", "n_cur", "kh", "vh", "n_hist",
+                 "nh", "hd", "scale", "mean", "o_local", "lse_local", "o_hist", "lse_hist",
+                 "o_full", "lse_full", "d_out", "ws", "ws_bytes", "stream"]
+        args = list(base)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(hd=64) == UNSUP
+    assert call(ws=0) == WS
+    assert call(ws_bytes=need - 1) == WS
+    assert call(mean=MIS) == ALIGN
+    assert call(ws=MIS) == ALIGN
+    assert call(q=0) == NULL
+    assert call(o_local=0, o_full=0) == NULL
+    assert call(scale=-1.0) == SHAPE
+    assert call(n_sink=0, n_cur=0) == SHAPE
+    assert call(n_q=0, ws=0, ws_bytes=0) == OK
+    km = _lib.lib.ispa_key_mean
+    kw = ispa.ispa_key_mean_workspace_bytes(2, 128)
+    assert kw > 0 and ispa.ispa_key_mean_workspace_bytes(2, 64) == 0
+    assert km(A, 10, A, 20, A, 30, 2, 128, 0, A, kw, 0) == NULL
+    assert km(0, 10, A, 20, A, 30, 2, 128, A, A, kw, 0) == NULL
+    assert km(A, 0, A, 0, A, 0, 2, 128, A, A, kw, 0) == SHAPE
+    assert km(A, 10, 0, 0, 0, 0, 2, 64, A, A, kw, 0) == UNSUP
+    assert km(A, 10, 0, 0, 0, 0, 2, 128, A, A, kw - 1, 0) == WS
+    assert km(MIS, 10, 0, 0, 0, 0, 2, 128, A, A, kw, 0) == ALIGN
+
+
 def test_w8a8_validation():
     """Argument checks of the W8A8 calls that return before any launch."""
     qz = _lib.lib.ispa_quantize_fp8
