@@ -396,6 +396,68 @@ def quantized_measure(ispa, w: wl.Workload, reps: int = 10, seed: int = 3):
     }
 
 
+def multi_instance_measure(ispa, w: wl.Workload, n_inst: int = 8, n_q: int = 512,
+                           reps: int = 5, seed: int = 4):
+    """Concurrent streams with their own KV and their own W + dW: n_inst
+    short chunks (n_q queries each, the workload's heads, sink and longest
+    warmup history) as separate calls and as one grouped call, for the
+    attention (O_full) and the output projection. HIP events on the launch
+    stream."""
+    dev, bf = "cuda", torch.bfloat16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    nh, d, h = w.n_heads, w.head_dim, w.hidden
+    n_hist = w.hist_per_step[-1]
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(*shape, device=dev, generator=gen) * std).to(bf)
+
+    calls = [dict(q=rnd(n_q, nh, d), k_sink=rnd(w.n_sink, nh, d), v_sink=rnd(w.n_sink, nh, d),
+                  k_cur=rnd(n_q, nh, d), v_cur=rnd(n_q, nh, d), k_hist=rnd(n_hist, nh, d),
+                  v_hist=rnd(n_hist, nh, d), o_full=torch.empty(n_q, h, dtype=bf, device=dev))
+             for _ in range(n_inst)]
+    xs = [rnd(n_q, h, std=0.3) for _ in range(n_inst)]
+    ws = [rnd(h, h, std=h ** -0.5) for _ in range(n_inst)]
+    ys = [torch.empty(n_q, h, dtype=bf, device=dev) for _ in range(n_inst)]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def attn_sep():
+        for c in calls:
+            ispa.ispa_attn_decomp(c["q"], c["k_sink"], c["v_sink"], c["k_cur"], c["v_cur"],
+                                  c["k_hist"], c["v_hist"], w.sm_scale, o_full=c["o_full"])
+
+    def proj_sep():
+        for x, wo, y in zip(xs, ws, ys):
+            ispa.ispa_project(x, wo, y)
+
+    t_as = timed(attn_sep)
+    t_ag = timed(lambda: ispa.ispa_attn_decomp_grouped(calls, w.sm_scale))
+    t_ps = timed(proj_sep)
+    t_pg = timed(lambda: ispa.ispa_project_grouped(xs, ws, ys))
+    fl = attn_flops(n_q, w.n_sink + n_q + n_hist, h) * n_inst
+    return {
+        "instances": n_inst,
+        "chunk": f"{n_q} queries x {nh} heads, {w.n_sink} + {n_q} local + {n_hist} history keys",
+        "attn_separate_ms": round(t_as, 3),
+        "attn_grouped_ms": round(t_ag, 3),
+        "attn_grouped_speedup": round(t_as / t_ag, 3),
+        "attn_grouped_tflops": round(fl / (t_ag * 1e-3) / 1e12, 1),
+        "proj_separate_us": round(t_ps * 1e3, 1),
+        "proj_grouped_us": round(t_pg * 1e3, 1),
+        "proj_grouped_speedup": round(t_ps / t_pg, 3),
+    }
+
+
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -727,6 +789,9 @@ def main():
     torch.cuda.empty_cache()
     print("[bench] E4M3 attention and W8A8 projection", file=sys.stderr, flush=True)
     out["quantized"] = quantized_measure(ispa, w)
+    torch.cuda.empty_cache()
+    print("[bench] grouped launches of concurrent instances", file=sys.stderr, flush=True)
+    out["multi_instance"] = multi_instance_measure(ispa, w)
     torch.cuda.empty_cache()
     if not a.no_stream:
         out["stream"] = stream_measure(ispa, w)

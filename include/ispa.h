@@ -96,6 +96,45 @@ int ispa_attn_decomp(const void* q, int64_t n_q,
                      void* d_out, void* stream);
 
 /*
+ * Several attention calls in one launch (multi-instance batching: concurrent
+ * streams, each with its own KV cache, as the paper's §3.3 instance-specific
+ * state implies when several videos are generated at once). Each job is
+ * one ispa_attn_decomp call with its own queries, KV segments, lengths and
+ * outputs; n_heads, head_dim and sm_scale are shared. Every job is
+ * validated as ispa_attn_decomp validates its arguments (the first failing
+ * job's status is returned and nothing is launched); jobs with n_q = 0 are
+ * skipped. 1 <= n_jobs <= ISPA_MAX_GROUP (ISPA_ERR_SHAPE otherwise). The
+ * results are bit-identical to separate ispa_attn_decomp calls. Calls whose
+ * own grid covers at least half the device's compute units run as launches
+ * of their own; the others share one launch (the case grouping is for:
+ * short chunks or few heads, each of which alone leaves most of the chip
+ * idle).
+ */
+#define ISPA_MAX_GROUP 8
+typedef struct {
+  const void* q;
+  int64_t n_q;
+  const void* k_sink;
+  const void* v_sink;
+  int64_t n_sink;
+  const void* k_cur;
+  const void* v_cur;
+  int64_t n_cur;
+  const void* k_hist;
+  const void* v_hist;
+  int64_t n_hist;
+  void* o_local;
+  float* lse_local;
+  void* o_hist;
+  float* lse_hist;
+  void* o_full;
+  float* lse_full;
+  void* d_out;
+} ispa_attn_job;
+int ispa_attn_decomp_grouped(const ispa_attn_job* jobs, int n_jobs, int n_heads, int head_dim,
+                             float sm_scale, void* stream);
+
+/*
  * Decomposable attention with E4M3 scores (§3.4 builds on FlashAttention-
  * style LSE states and cites SageAttention's 8-bit attention; §4.4 runs
  * ISPA with 8-bit quantization). Same arguments, outputs, split and merge
@@ -230,6 +269,25 @@ int ispa_apply_dW(int n_layers, int h, const int* selected, const float* dW,
  */
 int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in,
                  int h_out, void* stream);
+
+/*
+ * Several output projections in one launch (multi-instance batching: each
+ * instance has its own W + dW, §3.3's instance-specific update): job g
+ * computes y [n, h_out] = x [n, h_in] w^T as ispa_project does, with its
+ * own x, w (bf16 [h_out, h_in]) and y; h_in and h_out are shared.
+ * 1 <= n_jobs <= ISPA_MAX_GROUP and n >= 0 (ISPA_ERR_SHAPE);
+ * h_in % 32 == 0, h_out % 8 == 0, and each x and w below 2^31 bytes
+ * (ISPA_ERR_UNSUPPORTED); ISPA_ERR_NULL / ISPA_ERR_ALIGN for a job with
+ * n > 0. Results are bit-identical to separate ispa_project calls.
+ */
+typedef struct {
+  const void* x;
+  const void* w;
+  void* y;
+  int64_t n;
+} ispa_project_job;
+int ispa_project_grouped(const ispa_project_job* jobs, int n_jobs, int h_in, int h_out,
+                         void* stream);
 
 /*
  * W8A8 output projection (§4.4, "Compatibility with Post-Training

@@ -11,14 +11,15 @@ from ._lib import (EXPORTED, IspaError, KVCache, KVView, Session, SessionConfig,
                    ispa_drift_workspace_bytes, ispa_gram_accumulate, ispa_layer_score,
                    ispa_project, ispa_project_w8a8, ispa_project_w8a8_workspace_bytes,
                    ispa_quantize_fp8, ispa_attn_decomp_fp8, ispa_attn_fp8_workspace_bytes,
-                   ispa_key_mean, ispa_key_mean_workspace_bytes, ispa_ridge_solve, ispa_ridge_workspace_bytes,
+                   ispa_key_mean, ispa_key_mean_workspace_bytes, ispa_attn_decomp_grouped,
+                   ispa_project_grouped, ispa_ridge_solve, ispa_ridge_workspace_bytes,
                    ispa_status_string, ispa_version, lib)
 
 __all__ = ["IspaError", "KVCache", "KVView", "Session", "SessionConfig", "SessionState",
            "ispa_drift_prepare", "ispa_drift_score", "ispa_drift_workspace_bytes",
            "ispa_quantize_fp8", "ispa_project_w8a8", "ispa_project_w8a8_workspace_bytes",
            "ispa_attn_decomp_fp8", "ispa_attn_fp8_workspace_bytes", "ispa_key_mean",
-           "ispa_key_mean_workspace_bytes",
+           "ispa_key_mean_workspace_bytes", "ispa_attn_decomp_grouped", "ispa_project_grouped",
            "ispa_attn_decomp", "ispa_gram_accumulate",
            "ispa_ridge_solve", "ispa_ridge_workspace_bytes", "ispa_layer_score", "ispa_apply_dW",
            "ispa_project", "ispa_status_string", "ispa_version", "EXPORTED", "lib"]

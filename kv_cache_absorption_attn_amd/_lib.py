@@ -51,6 +51,33 @@ lib.ispa_key_mean_workspace_bytes.restype = _sz
 lib.ispa_key_mean_workspace_bytes.argtypes = [_i, _i]
 lib.ispa_key_mean.restype = _i
 lib.ispa_key_mean.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i, _i, _p, _p, _sz, _p]
+
+
+class AttnJob(ct.Structure):
+    """ispa_attn_job: one call of a grouped attention launch."""
+    _fields_ = [("q", ct.c_void_p), ("n_q", ct.c_int64),
+                ("k_sink", ct.c_void_p), ("v_sink", ct.c_void_p),
+                ("n_sink", ct.c_int64),
+                ("k_cur", ct.c_void_p), ("v_cur", ct.c_void_p), ("n_cur", ct.c_int64),
+                ("k_hist", ct.c_void_p), ("v_hist", ct.c_void_p),
+                ("n_hist", ct.c_int64),
+                ("o_local", ct.c_void_p), ("lse_local", ct.c_void_p),
+                ("o_hist", ct.c_void_p), ("lse_hist", ct.c_void_p),
+                ("o_full", ct.c_void_p), ("lse_full", ct.c_void_p),
+                ("d_out", ct.c_void_p)]
+
+
+class ProjectJob(ct.Structure):
+    """ispa_project_job: one product of a grouped projection launch."""
+    _fields_ = [("x", ct.c_void_p), ("w", ct.c_void_p), ("y", ct.c_void_p),
+                ("n", ct.c_int64)]
+
+
+MAX_GROUP = 8
+lib.ispa_attn_decomp_grouped.restype = _i
+lib.ispa_attn_decomp_grouped.argtypes = [ct.POINTER(AttnJob), _i, _i, _i, _f, _p]
+lib.ispa_project_grouped.restype = _i
+lib.ispa_project_grouped.argtypes = [ct.POINTER(ProjectJob), _i, _i, _i, _p]
 lib.ispa_gram_accumulate.restype = _i
 lib.ispa_gram_accumulate.argtypes = [_p, _p, _i64, _i, _i, _p, _p, _p, _i, _p]
 lib.ispa_ridge_workspace_bytes.restype = _sz
@@ -158,7 +185,8 @@ EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram
             "ispa_session_layer", "ispa_session_end_chunk", "ispa_session_query",
             "ispa_quantize_fp8", "ispa_project_w8a8_workspace_bytes", "ispa_project_w8a8",
             "ispa_attn_fp8_workspace_bytes", "ispa_attn_decomp_fp8",
-            "ispa_key_mean_workspace_bytes", "ispa_key_mean")
+            "ispa_key_mean_workspace_bytes", "ispa_key_mean", "ispa_attn_decomp_grouped",
+            "ispa_project_grouped")
 
 
 class IspaError(RuntimeError):
@@ -235,6 +263,50 @@ def ispa_attn_decomp(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: 
     st = lib.ispa_attn_decomp(_ptr(q, torch.bfloat16, "q"), n_q, *segs, n_heads, head_dim,
                               float(sm_scale), *outs, _stream(stream))
     _check("ispa_attn_decomp", st)
+
+
+def ispa_attn_decomp_grouped(calls, sm_scale: float, *, stream=None) -> None:
+    """Several attention calls in one launch. `calls` is a list of dicts with
+    the arguments of ispa_attn_decomp: q, k_sink, v_sink, k_cur, v_cur,
+    k_hist, v_hist and any of the outputs (same heads and head_dim)."""
+    if not 1 <= len(calls) <= MAX_GROUP:
+        raise ValueError(f"ispa_attn_decomp_grouped: 1..{MAX_GROUP} calls")
+    jobs = (AttnJob * len(calls))()
+    shape = None
+    for j, c in zip(jobs, calls):
+        q = c["q"]
+        if shape is not None and q.shape[1:] != shape:
+            raise ValueError("ispa_attn_decomp_grouped: heads / head_dim differ between calls")
+        shape = q.shape[1:]
+        n_q, _, _, segs, outs = _attn_args(
+            q, c.get("k_sink"), c.get("v_sink"), c.get("k_cur"), c.get("v_cur"),
+            c.get("k_hist"), c.get("v_hist"),
+            tuple(c.get(k) for k in ("o_local", "lse_local", "o_hist", "lse_hist", "o_full",
+                                     "lse_full", "d_out")))
+        j.q, j.n_q = _ptr(q, torch.bfloat16, "q"), n_q
+        j.k_sink, j.v_sink, j.n_sink, j.k_cur, j.v_cur, j.n_cur, j.k_hist, j.v_hist, \
+            j.n_hist = segs
+        j.o_local, j.lse_local, j.o_hist, j.lse_hist, j.o_full, j.lse_full, j.d_out = outs
+    st = lib.ispa_attn_decomp_grouped(jobs, len(calls), shape[0], shape[1], float(sm_scale),
+                                      _stream(stream))
+    _check("ispa_attn_decomp_grouped", st)
+
+
+def ispa_project_grouped(xs, ws, ys, *, stream=None) -> None:
+    """ys[g] [n_g, h_out] = xs[g] [n_g, h_in] ws[g]^T for every g, one launch."""
+    if not 1 <= len(xs) <= MAX_GROUP or not len(xs) == len(ws) == len(ys):
+        raise ValueError(f"ispa_project_grouped: 1..{MAX_GROUP} products")
+    h_out, h_in = ws[0].shape
+    jobs = (ProjectJob * len(xs))()
+    for j, x, w, y in zip(jobs, xs, ws, ys):
+        if tuple(w.shape) != (h_out, h_in) or x.shape[1] != h_in or \
+                tuple(y.shape) != (x.shape[0], h_out):
+            raise ValueError("ispa_project_grouped: shape mismatch")
+        j.x, j.w, j.y = (_ptr(x, torch.bfloat16, "x"), _ptr(w, torch.bfloat16, "w"),
+                         _ptr(y, torch.bfloat16, "y"))
+        j.n = x.shape[0]
+    st = lib.ispa_project_grouped(jobs, len(xs), h_in, h_out, _stream(stream))
+    _check("ispa_project_grouped", st)
 
 
 def ispa_attn_fp8_workspace_bytes(n_q: int, n_sink: int, n_cur: int, n_hist: int,

@@ -201,8 +201,9 @@ __device__ __forceinline__ void load_o(const uint16_t* in, f32x16* o, int64_t qi
   }
 }
 
+// One workgroup's work item `work` (head x query tile) of one attention call.
 template <int D, bool F8>
-__global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnParams p) {
+__device__ __forceinline__ void attn_block(const AttnParams& p, const int work) {
   static_assert(!F8 || D == 128, "the E4M3 instance is built for head_dim 128");
   constexpr int TBUF = kKTile * D;   // one V tile (elements)
   constexpr int KD = F8 ? D / 2 : D; // K tile row in 16-bit units
@@ -230,7 +231,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
   const int wave = tid / 64, lane = tid % 64, l32 = lane % 32, hf = lane / 32;
   const int pair = wave % kPairs;
   const bool s_role = wave < kPairs;
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int head = work / p.n_qtiles;
   const int qt = work % p.n_qtiles;
   const int64_t rs = static_cast<int64_t>(p.n_heads) * D;
@@ -713,8 +713,60 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnPara
   }
 }
 
+template <int D, bool F8>
+__global__ __launch_bounds__(kThreads, 1) void attn_decomp_kernel(const AttnParams p) {
+  attn_block<D, F8>(p, xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// Several attention calls (instances, same heads) in one launch. The
+// logical work order is head-major: for each head, the query tiles of call
+// 0, then of call 1, ... (start[g] = query tiles of the calls before g).
+// With the XCD remap each XCD takes a contiguous run of that order, so a
+// head's query tiles of one call still share an XCD's L2, and every XCD
+// gets a mix of all calls (calls with long histories are not piled onto a
+// few XCDs).
+template <int D, bool F8>
+__global__ __launch_bounds__(kThreads, 1) void attn_grouped_kernel(const AttnGroup grp) {
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_head = grp.start[grp.n];
+  const int head = t / per_head, r = t % per_head;
+  int g = 0;
+#pragma unroll 1
+  while (g + 1 < grp.n && r >= grp.start[g + 1]) ++g;
+  attn_block<D, F8>(grp.p[g], head * grp.p[g].n_qtiles + (r - grp.start[g]));
+}
 
 }  // namespace
+
+hipError_t launch_attn_grouped(AttnGroup grp, int head_dim, hipStream_t stream) {
+  if (grp.n < 1 || grp.n > kMaxGroup) return hipErrorInvalidValue;
+  const bool f8 = grp.p[0].q8 != nullptr;
+  const int n_heads = grp.p[0].n_heads;
+  int64_t per_head = 0;
+  for (int g = 0; g < grp.n; ++g) {
+    AttnParams& p = grp.p[g];
+    if ((p.q8 != nullptr) != f8 || p.n_heads != n_heads) return hipErrorInvalidValue;
+    p.n_qtiles = static_cast<int>((p.n_q + kQTile - 1) / kQTile);
+    grp.start[g] = static_cast<int>(per_head);
+    per_head += p.n_qtiles;
+  }
+  grp.start[grp.n] = static_cast<int>(per_head);
+  if (per_head * n_heads > INT32_MAX) return hipErrorInvalidValue;
+  const int total = static_cast<int>(per_head * n_heads);
+  if (total == 0) return hipSuccess;
+  if (f8) {
+    if (head_dim != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_grouped_kernel<128, true>), dim3(total), dim3(kThreads), 0, stream,
+                       grp);
+  } else if (head_dim == 128) {
+    hipLaunchKernelGGL((attn_grouped_kernel<128, false>), dim3(total), dim3(kThreads), 0, stream,
+                       grp);
+  } else {
+    hipLaunchKernelGGL((attn_grouped_kernel<64, false>), dim3(total), dim3(kThreads), 0, stream,
+                       grp);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_decomp(AttnParams p, int head_dim, hipStream_t stream) {
   p.n_qtiles = static_cast<int>((p.n_q + kQTile - 1) / kQTile);

@@ -287,6 +287,46 @@ int ispa_attn_decomp(const void* q, int64_t n_q, const void* k_sink, const void*
   return hip_status(ispa::launch_attn_decomp(p, head_dim, as_stream(stream)));
 }
 
+int ispa_attn_decomp_grouped(const ispa_attn_job* jobs, int n_jobs, int n_heads, int head_dim,
+                             float sm_scale, void* stream) {
+  if (!jobs) return ISPA_ERR_NULL;
+  if (n_jobs < 1 || n_jobs > ISPA_MAX_GROUP) return ISPA_ERR_SHAPE;
+  ispa::AttnGroup grp{};
+  for (int g = 0; g < n_jobs; ++g) {
+    const ispa_attn_job& j = jobs[g];
+    if (j.n_q == 0) continue;  // nothing to compute (its outputs may be empty, i.e. NULL)
+    ispa::AttnParams p{};
+    bool run = false;
+    const int st = attn_setup(j.q, j.n_q, j.k_sink, j.v_sink, j.n_sink, j.k_cur, j.v_cur,
+                              j.n_cur, j.k_hist, j.v_hist, j.n_hist, n_heads, head_dim, sm_scale,
+                              j.o_local, j.lse_local, j.o_hist, j.lse_hist, j.o_full, j.lse_full,
+                              j.d_out, &p, &run);
+    if (st != ISPA_OK) return st;
+    if (run) grp.p[grp.n++] = p;
+  }
+  if (grp.n == 0) return ISPA_OK;
+  // A call whose own grid covers at least half the compute units runs as a
+  // launch of its own: grouping it saves little idle hardware and adds tail
+  // imbalance between calls of different lengths. The smaller calls share
+  // one launch.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return ISPA_ERR_HIP;
+  const hipStream_t s = as_stream(stream);
+  ispa::AttnGroup small{};
+  for (int g = 0; g < grp.n; ++g) {
+    const int64_t tiles = (grp.p[g].n_q + ispa::attn_q_tile_min() - 1) / ispa::attn_q_tile_min();
+    if (tiles * n_heads >= cus / 2)
+      ISPA_TRY(ispa::launch_attn_decomp(grp.p[g], head_dim, s));
+    else
+      small.p[small.n++] = grp.p[g];
+  }
+  if (small.n == 1) return hip_status(ispa::launch_attn_decomp(small.p[0], head_dim, s));
+  if (small.n == 0) return ISPA_OK;
+  return hip_status(ispa::launch_attn_grouped(small, head_dim, s));
+}
+
 size_t ispa_attn_fp8_workspace_bytes(int64_t n_q, int64_t n_sink, int64_t n_cur, int64_t n_hist,
                                      int n_heads, int head_dim) {
   if (n_q < 0 || n_sink < 0 || n_cur < 0 || n_hist < 0 || n_heads < 1 || head_dim != 128)
@@ -597,6 +637,25 @@ int ispa_project_w8a8(const void* x, const void* wq, const float* w_scale, void*
   return hip_status(ispa::launch_nt_gemm256_fp8(xq, sx, static_cast<const uint8_t*>(wq),
                                                 w_scale, static_cast<uint16_t*>(y), n, h_in,
                                                 h_out, s));
+}
+
+int ispa_project_grouped(const ispa_project_job* jobs, int n_jobs, int h_in, int h_out,
+                         void* stream) {
+  if (!jobs) return ISPA_ERR_NULL;
+  if (n_jobs < 1 || n_jobs > ISPA_MAX_GROUP || h_in < 1 || h_out < 1) return ISPA_ERR_SHAPE;
+  if (h_in % 32 != 0 || h_out % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(h_out) * h_in * 2 > INT32_MAX) return ISPA_ERR_UNSUPPORTED;
+  ispa::NtJob nj[ISPA_MAX_GROUP];
+  for (int g = 0; g < n_jobs; ++g) {
+    const ispa_project_job& j = jobs[g];
+    if (j.n < 0) return ISPA_ERR_SHAPE;
+    if (j.n > 0 && (!j.x || !j.w || !j.y)) return ISPA_ERR_NULL;
+    if (j.n * h_in * 2 > INT32_MAX) return ISPA_ERR_UNSUPPORTED;
+    if (j.n > 0 && (!aligned16(j.x) || !aligned16(j.w) || !aligned16(j.y))) return ISPA_ERR_ALIGN;
+    nj[g] = ispa::NtJob{static_cast<const uint16_t*>(j.x), static_cast<const uint16_t*>(j.w),
+                        static_cast<uint16_t*>(j.y), j.n};
+  }
+  return hip_status(ispa::launch_nt_gemm256_grouped(nj, n_jobs, h_in, h_out, as_stream(stream)));
 }
 
 int ispa_project(const void* x, const void* w, void* y, int64_t n, int h_in, int h_out,

@@ -37,6 +37,15 @@ struct AttnParams {
 };
 // Fills p.n_qtiles, then launches.
 hipError_t launch_attn_decomp(AttnParams p, int head_dim, hipStream_t stream);
+// Up to kMaxGroup calls with the same head_dim and precision in one launch
+// (the table travels as the kernel argument); fills n_qtiles and start.
+constexpr int kMaxGroup = 8;
+struct AttnGroup {
+  AttnParams p[kMaxGroup];
+  int start[kMaxGroup + 1];
+  int n;
+};
+hipError_t launch_attn_grouped(AttnGroup grp, int head_dim, hipStream_t stream);
 
 // E4M3 attention operands (head_dim 128).
 struct KeySegs {
@@ -150,6 +159,16 @@ hipError_t launch_nt_gemm256_bf16(const uint16_t* x, const uint16_t* w, uint16_t
 // E4M3 operands (contraction length a multiple of 64), scales per row of X
 // and per row of W, bf16 out.
 bool nt_gemm256_fp8_supported(int h_in);
+// Up to kMaxGroup bf16 products Y_g = X_g W_g^T with shared h_in (% 32 == 0)
+// and h_out in one launch; each X_g and W below 2^31 bytes.
+struct NtJob {
+  const uint16_t* x;
+  const uint16_t* w;
+  uint16_t* y;
+  int64_t n;
+};
+hipError_t launch_nt_gemm256_grouped(const NtJob* jobs, int n_jobs, int h_in, int h_out,
+                                     hipStream_t stream);
 hipError_t launch_nt_gemm256_fp8(const uint8_t* xq, const float* sx, const uint8_t* wq,
                                  const float* sw, uint16_t* y, int64_t n, int h_in, int h_out,
                                  hipStream_t stream);

@@ -53,6 +53,13 @@ struct NtArgs {
   const float* sw;
 };
 
+// The products of a grouped launch; the table travels as the kernel argument.
+struct NtGroup {
+  NtArgs p[kMaxGroup];
+  int start[kMaxGroup + 1];
+  int n;
+};
+
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
@@ -61,8 +68,9 @@ typedef int v4i32_t __attribute__((ext_vector_type(4)));
 // l holding 32 consecutive k of row l % 32 from k = 32 (l / 32)), and the
 // epilogue applies the row and column scales. Either way a stage row is 64
 // bytes, so loads, swizzle and LDS layout are the same.
+// One workgroup tile: logical tile index t (grouped order) of batch entry b.
 template <bool F32OUT, bool FP8>
-__global__ __launch_bounds__(kNtThreads, 1) void nt_gemm256_kernel(const NtArgs p) {
+__device__ __forceinline__ void nt_tile(const NtArgs& p, const int t, const int64_t b) {
   __shared__ __attribute__((aligned(16))) uint16_t sa0[kBM * kRowE], sa1[kBM * kRowE],
       sa2[kBM * kRowE], sa3[kBM * kRowE];
   __shared__ __attribute__((aligned(16))) uint16_t sb0[kBN * kRowE], sb1[kBN * kRowE],
@@ -76,14 +84,12 @@ __global__ __launch_bounds__(kNtThreads, 1) void nt_gemm256_kernel(const NtArgs 
   const int tiles_m = static_cast<int>((p.n + kBM - 1) / kBM);
   const int tiles_n = (p.h_out + kBN - 1) / kBN;
   // grouped order: kGroupM row tiles share each column panel of W in L2
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = kGroupM * tiles_n;
   const int g = t / per_group, first_m = g * kGroupM;
   const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
   const int tm = first_m + (t % per_group) % gm, tn = (t % per_group) / gm;
   const int64_t m0 = static_cast<int64_t>(tm) * kBM;
   const int n0 = tn * kBN;
-  const int64_t b = blockIdx.y;
 
   const int nk = p.h_in / kKs;
   const int nst = p.a2 ? 2 * nk : nk;
@@ -229,6 +235,22 @@ __global__ __launch_bounds__(kNtThreads, 1) void nt_gemm256_kernel(const NtArgs 
   }
 }
 
+template <bool F32OUT, bool FP8>
+__global__ __launch_bounds__(kNtThreads, 1) void nt_gemm256_kernel(const NtArgs p) {
+  nt_tile<F32OUT, FP8>(p, xcd_remap(blockIdx.x, gridDim.x), blockIdx.y);
+}
+
+// Several products (instances with their own A, W and Y; shared h_in, h_out)
+// in one launch: product g owns the tiles [start[g], start[g + 1]) of the
+// XCD-remapped grid.
+__global__ __launch_bounds__(kNtThreads, 1) void nt_gemm256_grouped_kernel(const NtGroup grp) {
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  int g = 0;
+#pragma unroll 1
+  while (g + 1 < grp.n && t >= grp.start[g + 1]) ++g;
+  nt_tile<false, false>(grp.p[g], t - grp.start[g], 0);
+}
+
 // Buffer-load offsets are 32-bit: the rows of A are run in blocks whose
 // bytes stay below 2^31 (each block a launch of its own), and W must fit
 // below 2^31 bytes as a whole.
@@ -274,6 +296,29 @@ hipError_t launch_nt_gemm256_fp8(const uint8_t* xq, const float* sx, const uint8
                                  hipStream_t stream) {
   NtArgs a{xq, nullptr, 0, wq, 0, y, 0, n, h_in, h_out, sx, sw};
   return launch_nt<false, true>(a, 1, stream);
+}
+
+hipError_t launch_nt_gemm256_grouped(const NtJob* jobs, int n_jobs, int h_in, int h_out,
+                                     hipStream_t stream) {
+  if (n_jobs < 1 || n_jobs > kMaxGroup || !nt_gemm256_supported(h_in)) return hipErrorInvalidValue;
+  const int64_t row_bytes = static_cast<int64_t>(h_in) * 2;
+  if (static_cast<int64_t>(h_out) * row_bytes > INT32_MAX) return hipErrorInvalidValue;
+  NtGroup grp{};
+  grp.n = n_jobs;
+  int64_t total = 0;
+  for (int g = 0; g < n_jobs; ++g) {
+    const NtJob& j = jobs[g];
+    if (j.n < 0 || j.n * row_bytes > INT32_MAX) return hipErrorInvalidValue;
+    grp.p[g] = NtArgs{j.x, nullptr, 0, j.w, 0, j.y, 0, j.n, h_in, h_out, nullptr, nullptr};
+    grp.start[g] = static_cast<int>(total);
+    total += ((j.n + kBM - 1) / kBM) * ((h_out + kBN - 1) / kBN);
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+  }
+  grp.start[n_jobs] = static_cast<int>(total);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(nt_gemm256_grouped_kernel, dim3(static_cast<unsigned>(total)),
+                     dim3(kNtThreads), 0, stream, grp);
+  return hipGetLastError();
 }
 
 hipError_t launch_nt_gemm256_split_f32(const uint16_t* hi, const uint16_t* lo, const uint16_t* w,

@@ -156,6 +156,38 @@ def test_fp8_attention_validation():
     assert km(MIS, 10, 0, 0, 0, 0, 2, 128, A, A, kw, 0) == ALIGN
 
 
+def test_grouped_validation():
+    """Argument checks of the grouped launches that return before any launch."""
+    L = _lib.lib
+    job = _lib.AttnJob(q=A, n_q=10, k_sink=A, v_sink=A, n_sink=5, k_cur=A, v_cur=A, n_cur=5,
+                       k_hist=0, v_hist=0, n_hist=0, o_full=A)
+    jobs = (_lib.AttnJob * 9)(*([job] * 9))
+    assert L.ispa_attn_decomp_grouped(None, 1, 2, 128, 0.1, 0) == NULL
+    assert L.ispa_attn_decomp_grouped(jobs, 0, 2, 128, 0.1, 0) == SHAPE
+    assert L.ispa_attn_decomp_grouped(jobs, 9, 2, 128, 0.1, 0) == SHAPE
+    assert L.ispa_attn_decomp_grouped(jobs, 2, 2, 96, 0.1, 0) == UNSUP
+    bad = (_lib.AttnJob * 2)(job, _lib.AttnJob(q=A, n_q=10, n_cur=5, k_cur=A, v_cur=A,
+                                               o_full=MIS))
+    assert L.ispa_attn_decomp_grouped(bad, 2, 2, 128, 0.1, 0) == ALIGN
+    nothing = (_lib.AttnJob * 2)(_lib.AttnJob(q=A, n_q=10, n_cur=5, k_cur=A, v_cur=A),
+                                 _lib.AttnJob(q=0, n_q=0, n_cur=5, k_cur=A, v_cur=A, o_full=A))
+    assert L.ispa_attn_decomp_grouped(nothing, 2, 2, 128, 0.1, 0) == NULL   # job 0: no output
+    empty = (_lib.AttnJob * 1)(_lib.AttnJob(q=0, n_q=0, n_cur=5, k_cur=A, v_cur=A, o_full=A))
+    assert L.ispa_attn_decomp_grouped(empty, 1, 2, 128, 0.1, 0) == OK      # skipped
+    pj = (_lib.ProjectJob * 9)(*([_lib.ProjectJob(x=A, w=A, y=A, n=4)] * 9))
+    assert L.ispa_project_grouped(None, 1, 128, 128, 0) == NULL
+    assert L.ispa_project_grouped(pj, 9, 128, 128, 0) == SHAPE
+    assert L.ispa_project_grouped(pj, 2, 100, 128, 0) == UNSUP
+    assert L.ispa_project_grouped(pj, 2, 128, 100, 0) == UNSUP
+    assert L.ispa_project_grouped(pj, 2, 65536, 65536, 0) == UNSUP       # W above 2^31 bytes
+    neg = (_lib.ProjectJob * 1)(_lib.ProjectJob(x=A, w=A, y=A, n=-1))
+    assert L.ispa_project_grouped(neg, 1, 128, 128, 0) == SHAPE
+    nul = (_lib.ProjectJob * 1)(_lib.ProjectJob(x=A, w=0, y=A, n=4))
+    assert L.ispa_project_grouped(nul, 1, 128, 128, 0) == NULL
+    mis = (_lib.ProjectJob * 1)(_lib.ProjectJob(x=A, w=A, y=MIS, n=4))
+    assert L.ispa_project_grouped(mis, 1, 128, 128, 0) == ALIGN
+
+
 def test_w8a8_validation():
     """Argument checks of the W8A8 calls that return before any launch."""
     qz = _lib.lib.ispa_quantize_fp8
