@@ -42,8 +42,8 @@ METRIC = "decomp-attention TFLOP/s (% bf16 MFMA peak) + \u0394W absorb ms/layer,
 # value; otherwise `traffic` is null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_gram_wan14b_warmup_hbm_traffic.md")
 KERNEL_SOURCES = {
-    "attn_decomp_kernel<128>": ["kv_cache_absorption_attn_amd/csrc/attn_decomp.hip",
-                                "kv_cache_absorption_attn_amd/csrc/device_common.h"],
+    "attn_decomp_kernel<128, false>": ["kv_cache_absorption_attn_amd/csrc/attn_decomp.hip",
+                                       "kv_cache_absorption_attn_amd/csrc/device_common.h"],
     "gram_kernel": ["kv_cache_absorption_attn_amd/csrc/gram.hip",
                     "kv_cache_absorption_attn_amd/csrc/device_common.h"],
 }
@@ -508,13 +508,13 @@ def pmc_summary(fetch_csv: str, write_csv: str, w: wl.Workload):
         # the calibration copy is the last large copy of the run (smaller
         # device-to-host reads of the results follow it)
         copy = [v for _, n, v in rows if "copyBuffer" in n and v > 1024][-1]
-        attn = [v for _, n, v in rows if "attn_decomp_kernel<128>" in n]
+        attn = [v for _, n, v in rows if "attn_decomp_kernel<128, false>" in n]
         attn = [v for i, v in enumerate(attn) if i % (n_warm + n_post) < n_warm]
         # each step: n_warm Gram launches of the warmup, then one G-only launch
         # (W_o^T W_o of the layer score), which is left out
         gram = [v for _, n, v in rows if "gram_kernel" in n]
         gram = [v for i, v in enumerate(gram) if i % (n_warm + 1) < n_warm]
-        return copy, {"attn_decomp_kernel<128>": attn, "gram_kernel": gram}
+        return copy, {"attn_decomp_kernel<128, false>": attn, "gram_kernel": gram}
 
     fc, fe = read(fetch_csv, "FETCH_SIZE")
     wc, wr = read(write_csv, "WRITE_SIZE")
@@ -569,7 +569,7 @@ def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
         agg[k] = (c + 1, t + dt)
     total = sum(t for _, t in agg.values())
     n_warm, n_post = w.n_steps * w.n_layers, w.n_layers
-    attn = [dt for _, n, dt in rows if "attn_decomp_kernel<128>" in n]
+    attn = [dt for _, n, dt in rows if "attn_decomp_kernel<128, false>" in n]
     warm = [dt for i, dt in enumerate(attn) if i % (n_warm + n_post) < n_warm]
     post = [dt for i, dt in enumerate(attn) if i % (n_warm + n_post) >= n_warm]
     gram = [dt for _, n, dt in rows if "gram_kernel" in n]
@@ -673,7 +673,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--no-stream", action="store_true",
-                    help="skip the long-horizon streaming comparison (ISPA vs all-full)")
+                    help="skip the measurements after the warmup step: the quantized variants, "
+                         "the grouped launches, the long-horizon streaming comparison (ISPA vs "
+                         "all-full) and the session")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB copy (reference for the HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -740,7 +742,7 @@ def main():
     gap = (eps[order[w.k_select]] - eps[order[w.k_select - 1]]
            if w.k_select < w.n_layers else None)
 
-    attn_traffic = recorded_traffic("attn_decomp_kernel<128>")
+    attn_traffic = recorded_traffic("attn_decomp_kernel<128, false>")
     kv_bytes = sum(nk * w.n_heads * w.head_dim * 2 * 2 for nk in n_kv) * w.n_layers
     out = {
         "metric": METRIC,
@@ -772,7 +774,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": attn_traffic,
-                     "kernel": "attn_decomp_kernel<128>",
+                     "kernel": "attn_decomp_kernel<128, false>",
                      "launches_per_step": n_launch,
                      "flop_per_launch_avg": attn_fl / n_launch},
         "attn_kv_stream_gbs": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
@@ -785,15 +787,15 @@ def main():
         "eps_gap_at_k": gap,
         "solve_info_nonzero": sum(1 for v in info if v != 0),
     }
-    del inp, ws, timing
-    torch.cuda.empty_cache()
-    print("[bench] E4M3 attention and W8A8 projection", file=sys.stderr, flush=True)
-    out["quantized"] = quantized_measure(ispa, w)
-    torch.cuda.empty_cache()
-    print("[bench] grouped launches of concurrent instances", file=sys.stderr, flush=True)
-    out["multi_instance"] = multi_instance_measure(ispa, w)
-    torch.cuda.empty_cache()
     if not a.no_stream:
+        del inp, ws, timing
+        torch.cuda.empty_cache()
+        print("[bench] E4M3 attention and W8A8 projection", file=sys.stderr, flush=True)
+        out["quantized"] = quantized_measure(ispa, w)
+        torch.cuda.empty_cache()
+        print("[bench] grouped launches of concurrent instances", file=sys.stderr, flush=True)
+        out["multi_instance"] = multi_instance_measure(ispa, w)
+        torch.cuda.empty_cache()
         out["stream"] = stream_measure(ispa, w)
         torch.cuda.empty_cache()
         out["session"] = session_measure(ispa, w)
