@@ -267,7 +267,7 @@ def stream_measure(ispa, w: wl.Workload, frames=(60, 120), reps: int = 2, seed: 
     return res
 
 
-def session_measure(ispa, w: wl.Workload, n_stream: int = 3, seed: int = 2):
+def session_measure(ispa, w: wl.Workload, n_stream: int = 3, seed: int = 2, flags: int = 0):
     """The 14B-class life cycle through the native streaming session
     (ispa_session_*): a fresh stream of t_warm warmup chunks (every layer
     dual-stream, Gram accumulation, projection), the transition (solve,
@@ -275,7 +275,9 @@ def session_measure(ispa, w: wl.Workload, n_stream: int = 3, seed: int = 2):
     streaming chunks with the drift check of the L-layers on. Per chunk the
     layer calls are timed with HIP events; end_chunk (which reads the
     selection or the drift scores back, so it waits for the stream) with
-    the host clock. K/V writes are outside the timed regions."""
+    the host clock. K/V writes are outside the timed regions. `flags` selects
+    the quantized variant (W8A8 projections, E4M3 attention while
+    streaming)."""
     dev, bf = "cuda", torch.bfloat16
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
@@ -293,8 +295,9 @@ def session_measure(ispa, w: wl.Workload, n_stream: int = 3, seed: int = 2):
     n_chunks = t_warm + n_stream
     sess = ispa.Session(wo, n_heads=nh, head_dim=d, n_sink=w.n_sink, n_cur=w.n_cur,
                         hist_capacity=n_chunks * w.n_cur, k_select=w.k_select, t_warm=t_warm,
-                        sm_scale=w.sm_scale, lam=w.lam, drift_threshold=1e30, drift_stride=16)
-    res = {"t_warm": t_warm, "warmup_chunk_ms": [], "stream_chunk_ms": [], "events": [],
+                        sm_scale=w.sm_scale, lam=w.lam, drift_threshold=1e30, drift_stride=16,
+                        flags=flags)
+    res = {"flags": flags, "t_warm": t_warm, "warmup_chunk_ms": [], "stream_chunk_ms": [], "events": [],
            "end_chunk_host_ms": [], "workspace_gb": round(sess.workspace.numel() / 1e9, 2)}
     try:
         for l in range(L):
@@ -799,6 +802,11 @@ def main():
         out["stream"] = stream_measure(ispa, w)
         torch.cuda.empty_cache()
         out["session"] = session_measure(ispa, w)
+        torch.cuda.empty_cache()
+        out["session_quantized"] = session_measure(
+            ispa, w, flags=ispa.SESSION_W8A8 | ispa.SESSION_FP8_ATTN)
+        s0, s1 = out["session"]["stream_chunk_ms"], out["session_quantized"]["stream_chunk_ms"]
+        out["session_quantized"]["stream_speedup_vs_bf16"] = round(sum(s0) / sum(s1), 3)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_rows)

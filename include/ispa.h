@@ -539,11 +539,27 @@ typedef struct ispa_session ispa_session;
 enum { ISPA_PHASE_WARMUP = 0, ISPA_PHASE_STREAM = 1 };
 enum { ISPA_EVENT_NONE = 0, ISPA_EVENT_ABSORBED = 1, ISPA_EVENT_RECALIBRATE = 2 };
 
+/* Session flags (the quantized variant, §4.4 and §3.4's cited 8-bit
+ * attention):
+ *  ISPA_SESSION_W8A8      every output projection runs as ispa_project_w8a8
+ *                         on E4M3 weights with one scale per output channel,
+ *                         quantized from the active bf16 weights whenever they
+ *                         change (creation, absorption, recalibration), so an
+ *                         L-layer's W + dW is folded in before quantization;
+ *                         needs n_heads * head_dim % 64 == 0.
+ *  ISPA_SESSION_FP8_ATTN  the streaming phase's attention runs as
+ *                         ispa_attn_decomp_fp8, smoothed by the layer's mean
+ *                         sink key (the current chunk's keys when n_sink is
+ *                         0), fixed at the layer's first streamed chunk; the
+ *                         warmup keeps bf16 attention for the statistics.
+ *                         head_dim 128 only. */
+enum { ISPA_SESSION_W8A8 = 1, ISPA_SESSION_FP8_ATTN = 2 };
+
 typedef struct ispa_session_config {
   int32_t n_layers, n_heads, head_dim;   /* head_dim 64 or 128 */
   int32_t k_select;                      /* layers absorbed per transition */
   int32_t t_warm;                        /* warmup chunks per calibration (>= 1) */
-  int32_t reserved;
+  int32_t flags;                         /* ISPA_SESSION_* bits, 0 = bf16 throughout */
   int64_t n_sink, n_cur, hist_capacity;  /* tokens; hist_capacity % n_cur == 0 */
   float sm_scale, lambda;
   double drift_threshold;                /* <= 0: never recalibrate */
@@ -559,9 +575,10 @@ typedef struct ispa_session_state {
 size_t ispa_session_workspace_bytes(const ispa_session_config* cfg);
 
 /* Create a session (and its KV cache) on the current device; copies wo into
- * w_active on `stream`. Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (invalid
- * configuration), ISPA_ERR_UNSUPPORTED, ISPA_ERR_WORKSPACE, ISPA_ERR_ALIGN,
- * and those of ispa_kv_create. */
+ * w_active on `stream` (and, with ISPA_SESSION_W8A8, quantizes it).
+ * Errors: ISPA_ERR_NULL, ISPA_ERR_SHAPE (invalid configuration or unknown
+ * flag bits), ISPA_ERR_UNSUPPORTED (head_dim, or a flag the shape does not
+ * allow), ISPA_ERR_WORKSPACE, ISPA_ERR_ALIGN, and those of ispa_kv_create. */
 int ispa_session_create(const ispa_session_config* cfg, const void* wo,
                         void* w_active, void* workspace, size_t ws_bytes,
                         void* stream, ispa_session** out);

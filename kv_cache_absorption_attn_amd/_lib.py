@@ -131,10 +131,14 @@ lib.ispa_drift_score.argtypes = [_i, _i, _p, _p, _p, _i64, _i64, _p, _p, _sz, _p
 class SessionConfig(ct.Structure):
     """Mirror of ispa_session_config (include/ispa.h)."""
     _fields_ = [("n_layers", ct.c_int32), ("n_heads", ct.c_int32), ("head_dim", ct.c_int32),
-                ("k_select", ct.c_int32), ("t_warm", ct.c_int32), ("reserved", ct.c_int32),
+                ("k_select", ct.c_int32), ("t_warm", ct.c_int32), ("flags", ct.c_int32),
                 ("n_sink", _i64), ("n_cur", _i64), ("hist_capacity", _i64),
                 ("sm_scale", ct.c_float), ("lam", ct.c_float), ("drift_threshold", ct.c_double),
                 ("drift_stride", _i64)]
+
+
+SESSION_W8A8 = 1        # ISPA_SESSION_W8A8: E4M3 projections
+SESSION_FP8_ATTN = 2    # ISPA_SESSION_FP8_ATTN: E4M3 attention while streaming
 
 
 class SessionState(ct.Structure):
@@ -578,10 +582,12 @@ class Session:
 
     def __init__(self, wo, *, n_heads: int, head_dim: int, n_sink: int, n_cur: int,
                  hist_capacity: int, k_select: int, t_warm: int, sm_scale: float, lam: float,
-                 drift_threshold: float = 0.0, drift_stride: int = 1, stream=None):
+                 drift_threshold: float = 0.0, drift_stride: int = 1, flags: int = 0,
+                 stream=None):
         n_layers = wo.shape[0]
-        self.cfg = SessionConfig(n_layers, n_heads, head_dim, k_select, t_warm, 0, n_sink, n_cur,
-                                 hist_capacity, sm_scale, lam, drift_threshold, drift_stride)
+        self.cfg = SessionConfig(n_layers, n_heads, head_dim, k_select, t_warm, flags, n_sink,
+                                 n_cur, hist_capacity, sm_scale, lam, drift_threshold,
+                                 drift_stride)
         nbytes = int(lib.ispa_session_workspace_bytes(ct.byref(self.cfg)))
         if nbytes == 0:
             raise IspaError("ispa_session_workspace_bytes", ISPA_ERR_SHAPE)

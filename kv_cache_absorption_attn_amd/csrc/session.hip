@@ -17,6 +17,10 @@
 //          score, and when one exceeds the threshold the session re-enters
 //          warmup: L-layers get W back and restart their history, and the
 //          statistics start over.
+// With ISPA_SESSION_W8A8 every projection runs on E4M3 codes of the active
+// weights (requantized whenever those change); with ISPA_SESSION_FP8_ATTN
+// the streaming phase's attention runs on E4M3 scores, smoothed by a fixed
+// per-layer key mean.
 
 #include <hip/hip_runtime.h>
 
@@ -39,6 +43,16 @@ struct Layout {
   uint16_t *x, *d, *o;
   int *info, *info_drift, *selected;
   double *eps_abs, *eps_rel, *ref, *score;
+  // quantized variant (present only with the matching flag)
+  uint8_t* wq;           // [n_layers][h, h] E4M3 codes of the active weights
+  float* wsc;            // [n_layers][h] their scales
+  void* proj_ws;         // ispa_project_w8a8 workspace
+  size_t proj_bytes;
+  void* attn_ws;         // ispa_attn_decomp_fp8 workspace (largest view)
+  size_t attn_bytes;
+  uint16_t* mu;          // [n_layers][h] bf16 smoothing vectors
+  void* mean_ws;         // ispa_key_mean workspace
+  size_t mean_bytes;
   size_t bytes;
 };
 
@@ -78,6 +92,23 @@ Layout layout(const ispa_session_config& c, void* base) {
   w.eps_rel = reinterpret_cast<double*>(take(L * sizeof(double)));
   w.ref = reinterpret_cast<double*>(take(L * sizeof(double)));
   w.score = reinterpret_cast<double*>(take(L * sizeof(double)));
+  if (c.flags & ISPA_SESSION_W8A8) {
+    w.wq = reinterpret_cast<uint8_t*>(take(h * h * L));
+    w.wsc = reinterpret_cast<float*>(take(h * L * sizeof(float)));
+    w.proj_bytes = ispa_project_w8a8_workspace_bytes(c.n_cur, static_cast<int>(h));
+    w.proj_ws = take(w.proj_bytes);
+  }
+  if (c.flags & ISPA_SESSION_FP8_ATTN) {
+    // a view splits sink + history + current into three segments in some
+    // way; one segment holding every key plus two of 64 bounds the codes,
+    // the per-segment tile padding and the alignment of any split
+    w.attn_bytes = ispa_attn_fp8_workspace_bytes(c.n_cur, c.n_sink + c.n_cur + c.hist_capacity,
+                                                 64, 64, c.n_heads, c.head_dim);
+    w.attn_ws = take(w.attn_bytes);
+    w.mu = reinterpret_cast<uint16_t*>(take(h * L * 2));
+    w.mean_bytes = ispa_key_mean_workspace_bytes(c.n_heads, c.head_dim);
+    w.mean_ws = take(w.mean_bytes);
+  }
   w.bytes = off;
   return w;
 }
@@ -86,7 +117,7 @@ bool valid_config(const ispa_session_config* c) {
   return c->n_layers >= 1 && c->n_heads >= 1 && c->n_cur >= 1 && c->n_sink >= 0 &&
          c->hist_capacity >= 0 && c->t_warm >= 1 && c->k_select >= 0 &&
          c->k_select <= c->n_layers && c->drift_stride >= 1 && c->sm_scale > 0.f &&
-         c->lambda >= 0.f;
+         c->lambda >= 0.f && (c->flags & ~(ISPA_SESSION_W8A8 | ISPA_SESSION_FP8_ATTN)) == 0;
 }
 
 }  // namespace
@@ -106,7 +137,56 @@ struct ispa_session {
   std::vector<int> is_local;     // host copy of the current selection
   std::vector<double> eps_rel;   // host copy of the last errors
   std::vector<double> score;     // host copy of the last drift scores
+  std::vector<int> mu_ready;     // smoothing vector of the layer computed
 };
+
+namespace {
+
+// E4M3 codes of every layer's active weights (ISPA_SESSION_W8A8).
+int requantize(ispa_session* s, void* stream) {
+  if (!(s->cfg.flags & ISPA_SESSION_W8A8)) return ISPA_OK;
+  return ispa_quantize_fp8(s->w, static_cast<int64_t>(s->cfg.n_layers) * s->h, s->h, s->ws.wq,
+                           s->ws.wsc, stream);
+}
+
+// y = x W_l^T through the active weights (bf16 or their E4M3 codes).
+int project_layer(ispa_session* s, int layer, const void* x, void* y, void* stream) {
+  const ispa_session_config& c = s->cfg;
+  if (c.flags & ISPA_SESSION_W8A8)
+    return ispa_project_w8a8(x, s->ws.wq + layer * s->hh, s->ws.wsc + static_cast<int64_t>(layer) * s->h, y,
+                             c.n_cur, s->h, s->h, s->ws.proj_ws, s->ws.proj_bytes, stream);
+  return ispa_project(x, s->w + layer * s->hh, y, c.n_cur, s->h, s->h, stream);
+}
+
+// Streaming-phase attention of one layer into ws.x: local (sink + current)
+// for an L-layer, full for an F-layer; E4M3 scores with ISPA_SESSION_FP8_ATTN.
+int stream_attention(ispa_session* s, int layer, const void* q, void* stream) {
+  const ispa_session_config& c = s->cfg;
+  const bool local = s->is_local[layer] != 0;
+  if (!(c.flags & ISPA_SESSION_FP8_ATTN))
+    return ispa_kv_attn(s->kv, layer, q, c.n_cur, c.sm_scale, local ? s->ws.x : nullptr, nullptr,
+                        nullptr, nullptr, local ? nullptr : s->ws.x, nullptr, nullptr, stream);
+  ispa_kv_view v;
+  int st = ispa_kv_view_of(s->kv, layer, &v);
+  if (st != ISPA_OK) return st;
+  uint16_t* mu = s->ws.mu + static_cast<int64_t>(layer) * s->h;
+  if (!s->mu_ready[layer]) {
+    st = c.n_sink > 0 ? ispa_key_mean(v.k_sink, c.n_sink, nullptr, 0, nullptr, 0, c.n_heads,
+                                      c.head_dim, mu, s->ws.mean_ws, s->ws.mean_bytes, stream)
+                      : ispa_key_mean(nullptr, 0, v.k_cur, c.n_cur, nullptr, 0, c.n_heads,
+                                      c.head_dim, mu, s->ws.mean_ws, s->ws.mean_bytes, stream);
+    if (st != ISPA_OK) return st;
+    s->mu_ready[layer] = 1;
+  }
+  if (local && !v.split_ok) return ISPA_ERR_UNSUPPORTED;
+  return ispa_attn_decomp_fp8(q, c.n_cur, v.seg_k[0], v.seg_v[0], v.seg_n[0], v.seg_k[1],
+                              v.seg_v[1], v.seg_n[1], v.seg_k[2], v.seg_v[2], v.seg_n[2],
+                              c.n_heads, c.head_dim, c.sm_scale, mu, local ? s->ws.x : nullptr,
+                              nullptr, nullptr, nullptr, local ? nullptr : s->ws.x, nullptr,
+                              nullptr, s->ws.attn_ws, s->ws.attn_bytes, stream);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -122,6 +202,9 @@ int ispa_session_create(const ispa_session_config* cfg, const void* wo, void* w_
   if (!cfg || !wo || !w_active || !workspace) return ISPA_ERR_NULL;
   if (!valid_config(cfg)) return ISPA_ERR_SHAPE;
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return ISPA_ERR_UNSUPPORTED;
+  if ((cfg->flags & ISPA_SESSION_FP8_ATTN) && cfg->head_dim != 128) return ISPA_ERR_UNSUPPORTED;
+  if ((cfg->flags & ISPA_SESSION_W8A8) && (cfg->n_heads * cfg->head_dim) % 64 != 0)
+    return ISPA_ERR_UNSUPPORTED;
   if (ws_bytes < layout(*cfg, nullptr).bytes) return ISPA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(wo) | reinterpret_cast<uintptr_t>(w_active) |
        reinterpret_cast<uintptr_t>(workspace)) & 15u)
@@ -137,6 +220,7 @@ int ispa_session_create(const ispa_session_config* cfg, const void* wo, void* w_
   s->is_local.assign(cfg->n_layers, 0);
   s->eps_rel.assign(cfg->n_layers, 0.0);
   s->score.assign(cfg->n_layers, 0.0);
+  s->mu_ready.assign(cfg->n_layers, 0);
   int st = ispa_kv_create(cfg->n_layers, cfg->n_heads, cfg->head_dim, cfg->n_sink, cfg->n_cur,
                           cfg->hist_capacity, &s->kv);
   if (st != ISPA_OK) {
@@ -149,6 +233,11 @@ int ispa_session_create(const ispa_session_config* cfg, const void* wo, void* w_
     ispa_kv_destroy(s->kv);
     delete s;
     return ISPA_ERR_HIP;
+  }
+  if ((st = requantize(s, stream)) != ISPA_OK) {
+    ispa_kv_destroy(s->kv);
+    delete s;
+    return st;
   }
   *out = s;
   return ISPA_OK;
@@ -167,7 +256,6 @@ int ispa_session_layer(ispa_session* s, int layer, const void* q, void* y, void*
   if (!s || !q || !y) return ISPA_ERR_NULL;
   const ispa_session_config& c = s->cfg;
   if (layer < 0 || layer >= c.n_layers) return ISPA_ERR_SHAPE;
-  const uint16_t* wl = s->w + layer * s->hh;
   if (s->phase == ISPA_PHASE_WARMUP) {
     // dual stream: X = O_local and D into the statistics, O_full projected
     int st = ispa_kv_attn(s->kv, layer, q, c.n_cur, c.sm_scale, s->ws.x, nullptr, nullptr,
@@ -177,9 +265,10 @@ int ispa_session_layer(ispa_session* s, int layer, const void* q, void* y, void*
                               s->ws.C + layer * s->hh, s->ws.E + layer * s->hh,
                               s->warm_count == 0 ? 1 : 0, stream);
     if (st != ISPA_OK) return st;
-    return ispa_project(s->ws.o, wl, y, c.n_cur, s->h, s->h, stream);
+    return project_layer(s, layer, s->ws.o, y, stream);
   }
-  int st = ispa_kv_layer_forward(s->kv, layer, q, c.n_cur, c.sm_scale, wl, s->ws.x, y, stream);
+  int st = stream_attention(s, layer, q, stream);
+  if (st == ISPA_OK) st = project_layer(s, layer, s->ws.x, y, stream);
   if (st != ISPA_OK || !s->is_local[layer] || c.drift_threshold <= 0.0) return st;
   return ispa_drift_score(1, s->h, s->ws.linv + layer * s->hh, s->ws.ref + layer, s->ws.x,
                           c.n_cur, c.drift_stride, s->ws.score + layer, s->ws.drift_ws,
@@ -208,6 +297,7 @@ int ispa_session_end_chunk(ispa_session* s, void* stream, int* event) {
                                         hipMemcpyDeviceToDevice, hs) != hipSuccess)
       st = ISPA_ERR_HIP;
     if (st == ISPA_OK) st = ispa_apply_dW(L, s->h, s->ws.selected, s->ws.dW, s->w, stream);
+    if (st == ISPA_OK) st = requantize(s, stream);
     if (st == ISPA_OK && c.drift_threshold > 0.0)
       st = ispa_drift_prepare(L, s->h, s->ws.G, c.lambda, c.n_cur * c.t_warm, s->ws.linv,
                               s->ws.ref, s->ws.info_drift, s->ws.ridge_ws, s->ws.ridge_bytes,
@@ -254,6 +344,7 @@ int ispa_session_end_chunk(ispa_session* s, void* stream, int* event) {
   if (hipMemcpyAsync(s->w, s->wo, static_cast<size_t>(s->hh) * L * 2, hipMemcpyDeviceToDevice,
                      hs) != hipSuccess)
     return ISPA_ERR_HIP;
+  if ((st = requantize(s, stream)) != ISPA_OK) return st;
   std::fill(s->is_local.begin(), s->is_local.end(), 0);
   s->phase = ISPA_PHASE_WARMUP;
   s->warm_count = 0;

@@ -277,6 +277,20 @@ def test_drift_and_session_validation():
     assert L.ispa_session_create(ct.byref(d96), A, A, A, n, 0, ct.byref(h)) == UNSUP
     assert L.ispa_session_create(ct.byref(cfg), A, A, A, n - 1, 0, ct.byref(h)) == WS
     assert L.ispa_session_create(ct.byref(cfg), MIS, A, A, n, 0, ct.byref(h)) == ALIGN
+    # quantized variant: unknown flag bits, head_dim 64 with E4M3 attention,
+    # and the workspace that the flags add
+    unk = _lib.SessionConfig(2, 2, 64, 1, 2, 4, 8, 16, 64, 0.125, 0.01, 4.0, 4)
+    assert L.ispa_session_workspace_bytes(ct.byref(unk)) == 0
+    assert L.ispa_session_create(ct.byref(unk), A, A, A, n, 0, ct.byref(h)) == SHAPE
+    f8 = _lib.SessionConfig(2, 2, 64, 1, 2, _lib.SESSION_FP8_ATTN, 8, 16, 64, 0.125, 0.01, 4.0, 4)
+    n8 = L.ispa_session_workspace_bytes(ct.byref(f8))
+    assert n8 > n
+    assert L.ispa_session_create(ct.byref(f8), A, A, A, n8, 0, ct.byref(h)) == UNSUP
+    q = _lib.SessionConfig(2, 1, 128, 1, 2, _lib.SESSION_W8A8 | _lib.SESSION_FP8_ATTN, 8, 16, 64,
+                           0.125, 0.01, 4.0, 4)
+    nq = L.ispa_session_workspace_bytes(ct.byref(q))
+    assert nq >= n + 2 * 128 * 128
+    assert L.ispa_session_create(ct.byref(q), A, A, A, nq - 1, 0, ct.byref(h)) == WS
     assert h.value is None
     st = _lib.SessionState()
     assert L.ispa_session_destroy(None) == NULL

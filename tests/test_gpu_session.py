@@ -78,7 +78,9 @@ class OracleSession:
     """The oracle's replay of the session: the same life cycle, decided on
     the oracle's own numbers."""
 
-    def __init__(self, wo, n_sink, scale, lam, k_select, t_warm, tau):
+    def __init__(self, wo, n_sink, scale, lam, k_select, t_warm, tau, quant=False):
+        self.quant = quant                   # W8A8 projections, E4M3 attention when streaming
+        self.mu = {}
         self.wo = [np.asarray(w, dtype=np.float64) for w in wo]
         self.L = len(wo)
         self.scale, self.lam, self.k, self.t_warm, self.tau = scale, lam, k_select, t_warm, tau
@@ -91,25 +93,45 @@ class OracleSession:
         self.stats = None
         self.drift = [0.0] * self.L
 
+    def proj(self, o, l):
+        if self.quant:
+            # the projection quantizes the bf16 activations the attention
+            # stores (its input is bf16): E4M3 codes amplify a bf16-level
+            # difference of their input into whole code steps
+            wq, ws = orc.quantize_rows(self.w[l])
+            return orc.project_w8a8(orc.bf16_round(o), wq, ws)
+        return orc.project(o, self.w[l])
+
     def layer(self, l, c, q, ks, vs, kc, vc):
+        empty = np.zeros((0,) + kc[c].shape[1:])
+        streaming_fp8 = self.quant and self.phase == "stream"
+        if streaming_fp8 and l not in self.mu:
+            self.mu[l] = orc.bf16_round(orc.key_mean(ks))   # the sink's mean key, fixed
         if self.local[l]:
-            k = np.concatenate([ks, kc[c]])
-            v = np.concatenate([vs, vc[c]])
-            o, _ = orc.multihead_attention(q, k, v, self.scale)
+            if streaming_fp8:
+                o = orc.decomposable_attention_fp8(q, ks, vs, kc[c], vc[c], empty, empty,
+                                                   self.scale, self.mu[l])["o_local"]
+            else:
+                k = np.concatenate([ks, kc[c]])
+                v = np.concatenate([vs, vc[c]])
+                o, _ = orc.multihead_attention(q, k, v, self.scale)
             x = orc.bf16_round(o)
             g, n_warm = self.stats[l]
             self.drift[l] = orc.drift_score(x, g, self.lam, n_warm)
-            return o, orc.project(o, self.w[l])
+            return o, self.proj(o, l)
         hist = list(range(self.first[l], c))
-        empty = np.zeros((0,) + kc[c].shape[1:])
         kh = np.concatenate([kc[i] for i in hist]) if hist else empty
         vh = np.concatenate([vc[i] for i in hist]) if hist else empty
-        r = orc.decomposable_attention(q, ks, vs, kc[c], vc[c], kh, vh, self.scale)
+        if streaming_fp8:
+            r = orc.decomposable_attention_fp8(q, ks, vs, kc[c], vc[c], kh, vh, self.scale,
+                                               self.mu[l])
+        else:
+            r = orc.decomposable_attention(q, ks, vs, kc[c], vc[c], kh, vh, self.scale)
         if self.phase == "warmup":
             x, d = orc.stored_activations(r["o_local"], r["o_full"])
             self.xs[l].append(x)
             self.ds[l].append(d)
-        return r["o_full"], orc.project(r["o_full"], self.w[l])
+        return r["o_full"], self.proj(r["o_full"], l)
 
     def end_chunk(self, c):
         if self.phase == "warmup":
@@ -153,7 +175,24 @@ def test_session_life_cycle_with_recalibration():
     chunk 4 starts a new scene, which drives the L-layer's drift score past
     the threshold; chunks 5-6 warm up again and chunk 7 streams under the
     new calibration."""
-    L, nh, d, ns, nc = 3, 2, 64, 64, 256
+    life_cycle(nh=2, d=64, flags=0, y_tol=O_RELFRO)
+
+
+def test_session_quantized_life_cycle():
+    """The same life cycle with W8A8 projections (E4M3 weights requantized
+    at creation, absorption and recalibration) and E4M3 attention in the
+    streaming phase (one head of 128), against the oracle's replay with its
+    own quantized attention and W8A8 projection: the same selections, events
+    and drift bounds. Y is held to 3e-2 relative Frobenius: the E4M3 codes
+    of the activations turn the attention's own bf16-level differences into
+    whole code steps (2^-3 relative) wherever a value sits near a rounding
+    boundary, and a row's scale moves with its largest element; on this
+    case that alone moves Y by up to ~2 % between two correct chains."""
+    life_cycle(nh=1, d=128, flags=ispa.SESSION_W8A8 | ispa.SESSION_FP8_ATTN, y_tol=3e-2)
+
+
+def life_cycle(nh, d, flags, y_tol):
+    L, ns, nc = 3, 64, 256
     h = nh * d
     scale, lam, K, t_warm, tau = 1.0 / np.sqrt(d), 1e-2, 1, 2, 4.0
     temps = [1.0, 0.5, 2.0]
@@ -169,12 +208,13 @@ def test_session_life_cycle_with_recalibration():
     vc = [[] for _ in range(L)]
     sess = ispa.Session(dev_bf16(np.stack(wo)), n_heads=nh, head_dim=d, n_sink=ns, n_cur=nc,
                         hist_capacity=16 * nc, k_select=K, t_warm=t_warm, sm_scale=scale,
-                        lam=lam, drift_threshold=tau, drift_stride=1)
-    ref = OracleSession(wo, ns, scale, lam, K, t_warm, tau)
+                        lam=lam, drift_threshold=tau, drift_stride=1, flags=flags)
+    ref = OracleSession(wo, ns, scale, lam, K, t_warm, tau, quant=flags != 0)
     try:
         for l in range(L):
             sess.cache.write(l, dev_bf16(ks[l]), dev_bf16(vs[l]), sink=True)
         events = []
+        worst = 0.0
         y = torch.empty((nc, h), dtype=torch.bfloat16, device="cuda")
         for c in range(n_chunks):
             sc = scene[1 if c >= shift_at else 0]
@@ -189,7 +229,8 @@ def test_session_life_cycle_with_recalibration():
                 torch.cuda.synchronize()
                 o_ref, y_ref = ref.layer(l, c, q, ks[l], vs[l], kc[l], vc[l])
                 err = relfro(host(y), y_ref)
-                assert err <= O_RELFRO, f"chunk {c} layer {l}: y rel fro {err}"
+                worst = max(worst, err)
+                assert err <= y_tol, f"chunk {c} layer {l}: y rel fro {err}"
             st, _, _, drift_run = sess.state()
             drift_ref = list(ref.drift)
             ev = sess.end_chunk()
@@ -203,6 +244,7 @@ def test_session_life_cycle_with_recalibration():
                 assert loc == [int(x) for x in ref.local]
                 for l in range(L):
                     assert abs(eps[l] - ref.eps[l]) <= 5e-2 * ref.eps[l] + 1e-6
+        log(f"largest y rel fro over the chunks and layers: {worst:.4f}")
         assert events == [0, 1, 0, 0, 2, 0, 1, 0]
         st, loc, _, _ = sess.state()
         assert st.n_calibrations == 2 and st.chunk == n_chunks and st.phase == 1
