@@ -200,7 +200,8 @@ def summarize_events(timing):
     return tot, n_attn
 
 
-def stream_measure(ispa, w: wl.Workload, frames=(60, 120), reps: int = 2, seed: int = 1):
+def stream_measure(ispa, w: wl.Workload, frames=(36, 60, 90, 120), reps: int = 2,
+                   seed: int = 1):
     """Long-horizon streaming after absorption (14B-class) through the KV
     cache (ispa_kv_*): chunks of 3 latent frames stream in and every
     full-history layer's history grows, chunk by chunk, to `frames` latent
@@ -604,6 +605,60 @@ def pmc_summary(fetch_csv: str, write_csv: str, w: wl.Workload):
     return "\n".join(lines) + "\n"
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16"
+
+
+def pmc_mfma_summary(csv_path: str, w: wl.Workload):
+    """Markdown table of matrix-core counters per launch of the attention and
+    Gram kernels from one rocprofv3 --pmc run of MFMA_COUNTERS over one step
+    of this script. GRBM_GUI_ACTIVE reads as the sum of the 8 XCDs' active
+    cycles, so the shader clock of a launch is GUI / 8 / duration, and the
+    matrix-pipe busy fraction is SQ_VALU_MFMA_BUSY_CYCLES (summed over all
+    SIMDs) / (GUI / 8 x SIMDs). The MFMA FLOP the hardware counted
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) is set against the algorithmic FLOP
+    (the excess is the padded rows of partial tiles)."""
+    vals: dict = {}
+    names: dict = {}
+    dur: dict = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            i = int(r["Dispatch_Id"])
+            k = (i, r["Counter_Name"])
+            vals[k] = vals.get(k, 0.0) + float(r["Counter_Value"])
+            names[i] = r["Kernel_Name"]
+            dur[i] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    simds, xcds = 256 * 4, 8
+    n_warm, n_post = w.n_steps * w.n_layers, w.n_layers
+    n_kv = [w.n_sink + w.n_cur + hs for hs in w.hist_per_step]
+    attn_ids = sorted(i for i, n in names.items() if "attn_decomp_kernel<128, false>" in n)
+    attn_ids = [i for j, i in enumerate(attn_ids) if j % (n_warm + n_post) < n_warm]
+    gram_ids = sorted(i for i, n in names.items() if "gram_kernel" in n)
+    gram_ids = [i for j, i in enumerate(gram_ids) if j % (w.n_layers + 1) < w.n_layers]
+    rows = [("attn_decomp_kernel<128, false>", attn_ids,
+             sum(attn_flops(w.n_q, nk, w.hidden) for nk in n_kv) / len(n_kv)),
+            ("gram_kernel", gram_ids, gram_flops(w.n_steps * w.n_q, w.hidden))]
+    run = "python3 $REPO/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-stream"
+    lines = [f"# Matrix-core counters per launch: attention and Gram kernels, {w.name}", "",
+             "Commands (run from the repository root on one MI355X):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp",
+             f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d $REPO/gpurun_out/pmc_mfma "
+             f"-o mfma -- {run}",
+             "python3 $REPO/bench.py --pmc-mfma-summary "
+             "$REPO/gpurun_out/pmc_mfma/mfma_counter_collection.csv", "```", "",
+             "| kernel | launches | matrix pipe busy | shader clock (GHz) | counted MFMA FLOP / "
+             "algorithmic |", "|---|---:|---:|---:|---:|"]
+    for name, ids, fl in rows:
+        if not ids:
+            continue
+        busy = sum(vals.get((i, "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0) for i in ids)
+        gui = sum(vals.get((i, "GRBM_GUI_ACTIVE"), 0.0) for i in ids) / xcds
+        ns = sum(dur[i] for i in ids)
+        mops = sum(vals.get((i, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), 0.0) for i in ids)
+        lines.append(f"| {name} | {len(ids)} | {100 * busy / (gui * simds):.1f} % | "
+                     f"{gui / ns:.2f} | {mops * 512 / (fl * len(ids)):.3f} |")
+    return "\n".join(lines) + "\n"
+
+
 def _short_kernel_name(n: str) -> str:
     n = n.replace("void ", "").replace("ispa::(anonymous namespace)::", "")
     if n.startswith("at::native") or "at::native" in n[:40]:
@@ -683,11 +738,21 @@ def cpu_baseline(w: wl.Workload, n_rows: int):
     closed-form absorb (ridge solve + error) at full hidden size."""
     import numpy as np
     from oracle import ispa_oracle as orc
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in info] or [1])
+        blas = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in info
+                         if p.get("user_api") == "blas") or blas
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):  # pragma: no cover
+        pass
     step = w.n_steps - 1
     st = wl.step_inputs(w, 0, step, n_q=n_rows)
     n_kv = w.n_sink + w.n_cur + w.hist_per_step[step]
@@ -711,8 +776,17 @@ def cpu_baseline(w: wl.Workload, n_rows: int):
     dw = orc.ridge_delta_w(g, c, wo, w.lam)
     orc.layer_error_from_stats(g, c, e, wo, dw, w.lam)
     t_abs = time.perf_counter() - t0
+    # one layer-step's statistics over a token sample (plain matrix products)
+    n_g = 1024
+    xg = rng.standard_normal((n_g, h))
+    dg = rng.standard_normal((n_g, h))
+    t0 = time.perf_counter()
+    orc.gram_statistics([xg], [dg])
+    t_gram = time.perf_counter() - t0
     return {"value": round(attn_tflops, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
+            "gram_tflops": round(gram_flops(n_g, h) / t_gram / 1e12, 4),
+            "gram_sample": f"{n_g} tokens x hidden {h}: {t_gram:.2f} s",
             "sample": (f"decomposable attention of {n_rows} query rows x {w.n_heads} heads at "
                        f"the last warmup step ({n_kv} keys; the oracle computes local, history "
                        f"and full attention separately, so it does ~2x the algorithmic FLOP "
@@ -737,12 +811,17 @@ def main():
                     help="also run a plain 1 GiB copy (reference for the HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-mfma-summary", metavar="MFMA_CSV",
+                    help="print the matrix-core counter summary of a rocprofv3 --pmc run and exit")
     ap.add_argument("--trace-summary", metavar="TRACE_CSV",
                     help="print the summary of a rocprofv3 --kernel-trace CSV and exit")
     a = ap.parse_args()
 
     if a.trace_summary:
         sys.stdout.write(trace_summary(a.trace_summary, wl.WORKLOADS[a.workload], 2))
+        return
+    if a.pmc_mfma_summary:
+        sys.stdout.write(pmc_mfma_summary(a.pmc_mfma_summary, wl.WORKLOADS[a.workload]))
         return
     if a.pmc_summary:
         sys.stdout.write(pmc_summary(a.pmc_summary[0], a.pmc_summary[1],
