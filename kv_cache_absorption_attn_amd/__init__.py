@@ -16,7 +16,8 @@ from ._lib import (EXPORTED, SESSION_FP8_ATTN, SESSION_W8A8, IspaError, KVCache,
                    ispa_project_grouped, ispa_ridge_solve, ispa_ridge_workspace_bytes,
                    ispa_status_string, ispa_version, lib)
 
-__all__ = ["SESSION_W8A8", "SESSION_FP8_ATTN", "IspaError", "KVCache", "KVView", "Session", "SessionConfig", "SessionState",
+__all__ = ["SESSION_W8A8", "SESSION_FP8_ATTN", "IspaError", "KVCache", "KVView", "Session",
+           "SessionConfig", "SessionState",
            "ispa_drift_prepare", "ispa_drift_score", "ispa_drift_workspace_bytes",
            "ispa_quantize_fp8", "ispa_project_w8a8", "ispa_project_w8a8_workspace_bytes",
            "ispa_attn_decomp_fp8", "ispa_attn_fp8_workspace_bytes", "ispa_key_mean",

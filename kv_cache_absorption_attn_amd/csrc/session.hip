@@ -153,8 +153,9 @@ int requantize(ispa_session* s, void* stream) {
 int project_layer(ispa_session* s, int layer, const void* x, void* y, void* stream) {
   const ispa_session_config& c = s->cfg;
   if (c.flags & ISPA_SESSION_W8A8)
-    return ispa_project_w8a8(x, s->ws.wq + layer * s->hh, s->ws.wsc + static_cast<int64_t>(layer) * s->h, y,
-                             c.n_cur, s->h, s->h, s->ws.proj_ws, s->ws.proj_bytes, stream);
+    return ispa_project_w8a8(x, s->ws.wq + layer * s->hh,
+                             s->ws.wsc + static_cast<int64_t>(layer) * s->h, y, c.n_cur, s->h,
+                             s->h, s->ws.proj_ws, s->ws.proj_bytes, stream);
   return ispa_project(x, s->w + layer * s->hh, y, c.n_cur, s->h, s->h, stream);
 }
 

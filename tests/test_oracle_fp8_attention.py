@@ -102,7 +102,8 @@ def test_tiles_start_at_segment_start_and_are_independent():
     np.testing.assert_array_equal(s2[1], 4.0 * s[1])
     # the last, partial tile (8 keys) has its own scale
     assert s.shape == (4, 2)
-    np.testing.assert_array_equal(s[3], np.max(np.abs(k[192:].astype(np.float32)), axis=(0, 2)) / np.float32(448))
+    last = np.max(np.abs(k[192:].astype(np.float32)), axis=(0, 2)) / np.float32(448)
+    np.testing.assert_array_equal(s[3], last)
 
 
 def test_reconstruction_within_half_ulp():
