@@ -589,6 +589,14 @@ ispa_kv_cache* ispa_session_cache(ispa_session* s);
  * y [n_cur, h] bf16 out. Errors of the calls it makes. */
 int ispa_session_layer(ispa_session* s, int layer, const void* q, void* y,
                        void* stream);
+/* The same layer of n concurrent sessions (multi-instance batching), with
+ * the same results as n ispa_session_layer calls: the streaming-phase
+ * sessions without flags run their attention as one grouped launch and
+ * their projections (each through its own active weights) as another; the
+ * others run one by one. The sessions must share n_heads, head_dim and
+ * n_cur (ISPA_ERR_SHAPE otherwise); 1 <= n <= ISPA_MAX_GROUP. */
+int ispa_session_layer_grouped(ispa_session* const* s, int n, int layer,
+                               const void* const* q, void* const* y, void* stream);
 /* End of a chunk; *event (may be NULL) receives ISPA_EVENT_*. */
 int ispa_session_end_chunk(ispa_session* s, void* stream, int* event);
 /* Phase and counters; with non-NULL host arrays of n_layers entries also

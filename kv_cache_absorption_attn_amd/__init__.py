@@ -13,7 +13,7 @@ from ._lib import (EXPORTED, SESSION_FP8_ATTN, SESSION_W8A8, IspaError, KVCache,
                    ispa_project, ispa_project_w8a8, ispa_project_w8a8_workspace_bytes,
                    ispa_quantize_fp8, ispa_attn_decomp_fp8, ispa_attn_fp8_workspace_bytes,
                    ispa_key_mean, ispa_key_mean_workspace_bytes, ispa_attn_decomp_grouped,
-                   ispa_project_grouped, ispa_ridge_solve, ispa_ridge_workspace_bytes,
+                   ispa_project_grouped, ispa_session_layer_grouped, ispa_ridge_solve, ispa_ridge_workspace_bytes,
                    ispa_status_string, ispa_version, lib)
 
 __all__ = ["SESSION_W8A8", "SESSION_FP8_ATTN", "IspaError", "KVCache", "KVView", "Session",
@@ -22,6 +22,7 @@ __all__ = ["SESSION_W8A8", "SESSION_FP8_ATTN", "IspaError", "KVCache", "KVView",
            "ispa_quantize_fp8", "ispa_project_w8a8", "ispa_project_w8a8_workspace_bytes",
            "ispa_attn_decomp_fp8", "ispa_attn_fp8_workspace_bytes", "ispa_key_mean",
            "ispa_key_mean_workspace_bytes", "ispa_attn_decomp_grouped", "ispa_project_grouped",
+           "ispa_session_layer_grouped",
            "ispa_attn_decomp", "ispa_gram_accumulate",
            "ispa_ridge_solve", "ispa_ridge_workspace_bytes", "ispa_layer_score", "ispa_apply_dW",
            "ispa_project", "ispa_status_string", "ispa_version", "EXPORTED", "lib"]

@@ -78,6 +78,8 @@ lib.ispa_attn_decomp_grouped.restype = _i
 lib.ispa_attn_decomp_grouped.argtypes = [ct.POINTER(AttnJob), _i, _i, _i, _f, _p]
 lib.ispa_project_grouped.restype = _i
 lib.ispa_project_grouped.argtypes = [ct.POINTER(ProjectJob), _i, _i, _i, _p]
+lib.ispa_session_layer_grouped.restype = _i
+lib.ispa_session_layer_grouped.argtypes = [_p, _i, _i, _p, _p, _p]
 lib.ispa_gram_accumulate.restype = _i
 lib.ispa_gram_accumulate.argtypes = [_p, _p, _i64, _i, _i, _p, _p, _p, _i, _p]
 lib.ispa_ridge_workspace_bytes.restype = _sz
@@ -190,7 +192,7 @@ EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram
             "ispa_quantize_fp8", "ispa_project_w8a8_workspace_bytes", "ispa_project_w8a8",
             "ispa_attn_fp8_workspace_bytes", "ispa_attn_decomp_fp8",
             "ispa_key_mean_workspace_bytes", "ispa_key_mean", "ispa_attn_decomp_grouped",
-            "ispa_project_grouped")
+            "ispa_project_grouped", "ispa_session_layer_grouped")
 
 
 class IspaError(RuntimeError):
@@ -684,3 +686,16 @@ def ispa_project_w8a8(x, wq, w_scale, y, workspace, *, stream=None) -> None:
                                _ptr(workspace, None, "workspace"),
                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ispa_project_w8a8", st)
+
+
+def ispa_session_layer_grouped(sessions, layer: int, qs, ys, *, stream=None) -> None:
+    """The same layer of several Session objects in grouped launches (the
+    results equal separate Session.layer calls)."""
+    n = len(sessions)
+    if not 1 <= n <= MAX_GROUP or len(qs) != n or len(ys) != n:
+        raise ValueError(f"ispa_session_layer_grouped: 1..{MAX_GROUP} sessions")
+    hs = (_p * n)(*[sess.handle for sess in sessions])
+    qp = (_p * n)(*[_ptr(q, torch.bfloat16, "q") for q in qs])
+    yp = (_p * n)(*[_ptr(y, torch.bfloat16, "y") for y in ys])
+    st = lib.ispa_session_layer_grouped(hs, n, layer, qp, yp, _stream(stream))
+    _check("ispa_session_layer_grouped", st)

@@ -276,6 +276,86 @@ int ispa_session_layer(ispa_session* s, int layer, const void* q, void* y, void*
                           s->ws.drift_bytes, stream);
 }
 
+int ispa_session_layer_grouped(ispa_session* const* s, int n, int layer, const void* const* q,
+                               void* const* y, void* stream) {
+  if (!s || !q || !y) return ISPA_ERR_NULL;
+  if (n < 1 || n > ISPA_MAX_GROUP) return ISPA_ERR_SHAPE;
+  for (int g = 0; g < n; ++g) {
+    if (!s[g] || !q[g] || !y[g]) return ISPA_ERR_NULL;
+    const ispa_session_config& a = s[g]->cfg;
+    const ispa_session_config& b = s[0]->cfg;
+    if (a.n_heads != b.n_heads || a.head_dim != b.head_dim || a.n_cur != b.n_cur ||
+        layer < 0 || layer >= a.n_layers)
+      return ISPA_ERR_SHAPE;
+  }
+  const ispa_session_config& c0 = s[0]->cfg;
+  ispa_attn_job jobs[ISPA_MAX_GROUP] = {};
+  ispa_project_job proj[ISPA_MAX_GROUP] = {};
+  int grouped[ISPA_MAX_GROUP];
+  int m = 0;
+  for (int g = 0; g < n; ++g) {
+    ispa_session* sg = s[g];
+    if (sg->phase != ISPA_PHASE_STREAM || sg->cfg.flags != 0) {
+      const int st = ispa_session_layer(sg, layer, q[g], y[g], stream);
+      if (st != ISPA_OK) return st;
+      continue;
+    }
+    ispa_kv_view v;
+    int st = ispa_kv_view_of(sg->kv, layer, &v);
+    if (st != ISPA_OK) return st;
+    const bool local = sg->is_local[layer] != 0;
+    if (local && !v.split_ok) return ISPA_ERR_UNSUPPORTED;
+    ispa_attn_job& j = jobs[m];
+    j.q = q[g];
+    j.n_q = sg->cfg.n_cur;
+    j.k_sink = v.seg_k[0];
+    j.v_sink = v.seg_v[0];
+    j.n_sink = v.seg_n[0];
+    j.k_cur = v.seg_k[1];
+    j.v_cur = v.seg_v[1];
+    j.n_cur = v.seg_n[1];
+    j.k_hist = v.seg_k[2];
+    j.v_hist = v.seg_v[2];
+    j.n_hist = v.seg_n[2];
+    (local ? j.o_local : j.o_full) = sg->ws.x;
+    proj[m] = ispa_project_job{sg->ws.x, sg->w + layer * sg->hh, y[g], sg->cfg.n_cur};
+    grouped[m++] = g;
+  }
+  if (m == 0) return ISPA_OK;
+  // the sessions share the softmax scale only if their configurations do
+  bool same_scale = true;
+  for (int k = 1; k < m; ++k)
+    same_scale &= s[grouped[k]]->cfg.sm_scale == s[grouped[0]]->cfg.sm_scale;
+  int st = ISPA_OK;
+  if (same_scale) {
+    st = ispa_attn_decomp_grouped(jobs, m, c0.n_heads, c0.head_dim, s[grouped[0]]->cfg.sm_scale,
+                                  stream);
+  } else {
+    for (int k = 0; k < m && st == ISPA_OK; ++k)
+      st = ispa_attn_decomp_grouped(&jobs[k], 1, c0.n_heads, c0.head_dim,
+                                    s[grouped[k]]->cfg.sm_scale, stream);
+  }
+  if (st != ISPA_OK) return st;
+  const int h = s[grouped[0]]->h;
+  if (h % 32 == 0) {
+    st = ispa_project_grouped(proj, m, h, h, stream);
+  } else {
+    for (int k = 0; k < m && st == ISPA_OK; ++k)
+      st = ispa_project(proj[k].x, proj[k].w, proj[k].y, proj[k].n, h, h, stream);
+  }
+  if (st != ISPA_OK) return st;
+  for (int k = 0; k < m; ++k) {
+    ispa_session* sg = s[grouped[k]];
+    const ispa_session_config& c = sg->cfg;
+    if (!sg->is_local[layer] || c.drift_threshold <= 0.0) continue;
+    st = ispa_drift_score(1, sg->h, sg->ws.linv + layer * sg->hh, sg->ws.ref + layer, sg->ws.x,
+                          c.n_cur, c.drift_stride, sg->ws.score + layer, sg->ws.drift_ws,
+                          sg->ws.drift_bytes, stream);
+    if (st != ISPA_OK) return st;
+  }
+  return ISPA_OK;
+}
+
 int ispa_session_end_chunk(ispa_session* s, void* stream, int* event) {
   if (!s) return ISPA_ERR_NULL;
   const ispa_session_config& c = s->cfg;

@@ -298,5 +298,13 @@ def test_drift_and_session_validation():
     assert L.ispa_session_layer(None, 0, A, A, 0) == NULL
     assert L.ispa_session_end_chunk(None, 0, None) == NULL
     assert L.ispa_session_query(None, ct.byref(st), None, None, None) == NULL
+    g = L.ispa_session_layer_grouped
+    ptrs = (ct.c_void_p * 9)(*([A] * 9))
+    nulls = (ct.c_void_p * 2)(None, None)
+    assert g(None, 1, 0, ptrs, ptrs, 0) == NULL
+    assert g(ptrs, 1, 0, None, ptrs, 0) == NULL
+    assert g(ptrs, 0, 0, ptrs, ptrs, 0) == SHAPE
+    assert g(ptrs, 9, 0, ptrs, ptrs, 0) == SHAPE
+    assert g(nulls, 2, 0, ptrs, ptrs, 0) == NULL     # a NULL session, never dereferenced
     assert ct.sizeof(_lib.SessionConfig) == 6 * 4 + 3 * 8 + 2 * 4 + 8 + 8
     assert ct.sizeof(_lib.SessionState) == 4 * 4 + 8

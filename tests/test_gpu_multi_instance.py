@@ -149,3 +149,56 @@ def test_grouped_mixed_large_and_small():
     gpu = {"o_local": host(c["o_local"])[rows], "o_full": host(c["o_full"])[rows],
            "d": host(c["d_out"])[rows], "lse_full": host(c["lse_full"])[:, rows]}
     compare_attention(gpu, ref)
+
+
+def test_grouped_sessions_match_single_sessions():
+    """Two concurrent sessions (own weights, own streams of K/V/Q) stepped
+    layer by layer through ispa_session_layer_grouped, beside twin sessions
+    stepped alone with ispa_session_layer: every output bit-identical, the
+    same events, through warmup, absorption and streaming (drift scores on,
+    threshold out of reach)."""
+    L, nh, d, ns, nc, t_warm, n_chunks = 3, 2, 64, 64, 256, 2, 5
+    h = nh * d
+    scale = 1.0 / np.sqrt(d)
+    rnd = lambda shape, seed, std=1.0: wl.random_bf16(shape, std, 7000 + seed)
+    kw = dict(n_heads=nh, head_dim=d, n_sink=ns, n_cur=nc, hist_capacity=8 * nc, k_select=1,
+              t_warm=t_warm, sm_scale=scale, lam=1e-2, drift_threshold=1e30, drift_stride=2)
+    wos = [dev_bf16(rnd((L, h, h), 100 * i, 1.0 / np.sqrt(h))) for i in range(2)]
+    grouped = [ispa.Session(wos[i], **kw) for i in range(2)]
+    alone = [ispa.Session(wos[i], **kw) for i in range(2)]
+    try:
+        for i in range(2):
+            for l in range(L):
+                k, v = dev_bf16(rnd((ns, nh, d), 10 * i + l)), dev_bf16(rnd((ns, nh, d), 50 + l))
+                grouped[i].cache.write(l, k, v, sink=True)
+                alone[i].cache.write(l, k, v, sink=True)
+        ys_g = [torch.empty((nc, h), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+        ys_a = [torch.empty((nc, h), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+        for c in range(n_chunks):
+            for i in range(2):
+                for l in range(L):
+                    k = dev_bf16(rnd((nc, nh, d), 1000 * c + 10 * i + l))
+                    v = dev_bf16(rnd((nc, nh, d), 1000 * c + 10 * i + l + 500))
+                    grouped[i].cache.write(l, k, v)
+                    alone[i].cache.write(l, k, v)
+            for l in range(L):
+                qs = [dev_bf16(rnd((nc, nh, d), 90000 + 100 * c + 10 * i + l, 0.5 + l))
+                      for i in range(2)]
+                ispa.ispa_session_layer_grouped(grouped, l, qs, ys_g)
+                for i in range(2):
+                    alone[i].layer(l, qs[i], ys_a[i])
+                torch.cuda.synchronize()
+                for i in range(2):
+                    assert torch.equal(ys_g[i], ys_a[i]), f"chunk {c} layer {l} session {i}"
+            ev_g = [sess.end_chunk() for sess in grouped]
+            ev_a = [sess.end_chunk() for sess in alone]
+            log(f"chunk {c}: events grouped {ev_g} alone {ev_a}")
+            assert ev_g == ev_a
+        for sg, sa in zip(grouped, alone):
+            st_g, loc_g, _, dr_g = sg.state()
+            st_a, loc_a, _, dr_a = sa.state()
+            assert loc_g == loc_a and st_g.phase == st_a.phase == 1
+            assert dr_g == dr_a
+    finally:
+        for sess in grouped + alone:
+            sess.close()
