@@ -1,5 +1,7 @@
 // Operand preparation of the E4M3 decomposable attention (the quantized
-// attention in the spirit of SageAttention, which the ISPA paper's §3.4
+// attention in the spirit of SageAttention, which the ISPA paper, "Towards
+// Memory-Efficient Autoregressive Video Generation via Instance-Specific
+// Parametric Absorption", §3.4
 // cites; §4.4 runs ISPA with 8-bit quantization): per-(token, head) query
 // codes with the LSE smoothing shift, per-(64-key tile, head) codes of the
 // smoothed keys, and the key mean used as the smoothing vector.

@@ -1,5 +1,7 @@
-// ISPA streaming session: the warmup -> absorption -> streaming life cycle of
-// all attention layers over one KV cache, with event-triggered
+// ISPA streaming session (the ISPA paper: "Towards Memory-Efficient
+// Autoregressive Video Generation via Instance-Specific Parametric
+// Absorption"). The warmup -> absorption -> streaming life cycle of all
+// attention layers over one KV cache, with event-triggered
 // recalibration (ISPA paper §3.1 items 1-3, §3.3 including its last
 // paragraph). Host-side control only: every step is a call of the C ABI in
 // include/ispa.h, enqueued on the caller's stream. Contracts are in

@@ -1,5 +1,7 @@
-// W8A8 output projection (ISPA paper §4.4, "Compatibility with Post-Training
-// Quantization": 8-bit weights and activations for the linear layers; for an
+// W8A8 output projection (the ISPA paper, "Towards Memory-Efficient
+// Autoregressive Video Generation via Instance-Specific Parametric
+// Absorption", §4.4, "Compatibility with Post-Training Quantization": 8-bit
+// weights and activations for the linear layers; for an
 // L-layer the update is folded in first, W_new = W + dW, then quantized).
 // Format: OCP 8-bit floating point E4M3 ("fn": bias 7, no infinities,
 // largest finite 448). Each row (an output channel of W, a token of X) gets
