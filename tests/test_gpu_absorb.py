@@ -399,6 +399,32 @@ def test_project(n, h_in, h_out):
     assert relfro(got, ref) <= 4e-3
 
 
+def test_project_input_above_2gib():
+    """X above 2^31 bytes (220000 tokens x 5120, 2.25 GB): buffer offsets are
+    32-bit, so the launch runs in row blocks below 2^31 bytes. The rows repeat
+    1021 seeded rows (a prime period, so a block that read from the wrong
+    offset would meet different rows); every 1021st-period row, and the rows
+    around each block boundary, against the oracle."""
+    n, h = 220000, 5120
+    period = 1021
+    log(f"project {n}x{h}->{h} (input above 2 GiB)")
+    base = wl.random_bf16((period, h), 0.5, 53)
+    wt = wl.random_bf16((h, h), 1.0 / np.sqrt(h), 54)
+    idx = torch.arange(n, device="cuda") % period
+    x = dev_bf16(base).index_select(0, idx)
+    y = torch.empty((n, h), dtype=torch.bfloat16, device="cuda")
+    ispa.ispa_project(x, dev_bf16(wt), y)
+    torch.cuda.synchronize()
+    del x
+    ref = orc.project(base, wt)
+    block = (2 ** 31 - 1) // (h * 2) // 256 * 256          # rows per launch
+    rows = sorted(set(range(0, n, 997)) | {r for b in range(block, n, block)
+                                          for r in (b - 1, b, b + 1) if r < n} | {n - 1})
+    got = host(y[torch.tensor(rows, device="cuda")])
+    exp = ref[np.array(rows) % period]
+    assert np.max(np.abs(got - exp) / (np.abs(exp) + 1e-3)) <= 2 ** -8 + 1e-3
+
+
 # ------------------------------------------------------------------ realistic conditioning
 
 def test_wan13_layer_warmup_ridge():
