@@ -666,6 +666,28 @@ def _short_kernel_name(n: str) -> str:
     return n.split("(")[0][:70]
 
 
+def trace_table(trace_csv: str, command: str):
+    """Markdown table of every kernel in a rocprofv3 --kernel-trace CSV:
+    launches, average and total time (the whole run, all measurement legs)."""
+    agg: dict = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            k = _short_kernel_name(r["Kernel_Name"])
+            c, t = agg.get(k, (0, 0))
+            agg[k] = (c + 1, t + int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = sum(t for _, t in agg.values())
+    lines = ["Command (run from the repository root on one MI355X):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp", command,
+             "python3 $REPO/bench.py --trace-table $REPO/gpurun_out/ktq/ktq_kernel_trace.csv",
+             "```", "", "| Kernel | Calls | Avg (us) | Total (ms) | % |",
+             "|---|---:|---:|---:|---:|"]
+    for k, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        if t / total < 1e-4:
+            continue
+        lines.append(f"| {k} | {c} | {t / c / 1e3:.1f} | {t / 1e6:.2f} | {100 * t / total:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
     """Markdown summary of a rocprofv3 --kernel-trace CSV of `passes` steps of
     this script: per-kernel totals, and the attention launches split into the
@@ -813,10 +835,18 @@ def main():
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--pmc-mfma-summary", metavar="MFMA_CSV",
                     help="print the matrix-core counter summary of a rocprofv3 --pmc run and exit")
+    ap.add_argument("--trace-table", metavar="TRACE_CSV",
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace CSV and exit")
     ap.add_argument("--trace-summary", metavar="TRACE_CSV",
                     help="print the summary of a rocprofv3 --kernel-trace CSV and exit")
     a = ap.parse_args()
 
+    if a.trace_table:
+        sys.stdout.write(trace_table(
+            a.trace_table, "rocprofv3 --kernel-trace --stats --output-format csv -d "
+            "$REPO/gpurun_out/ktq -o ktq -- python3 $REPO/bench.py --steps 1 --warmup 0 "
+            "--no-cpu-baseline"))
+        return
     if a.trace_summary:
         sys.stdout.write(trace_summary(a.trace_summary, wl.WORKLOADS[a.workload], 2))
         return
