@@ -155,7 +155,8 @@ int ispa_attn_decomp_grouped(const ispa_attn_job* jobs, int n_jobs, int n_heads,
  * workspace        ispa_attn_fp8_workspace_bytes(n_q, n_sink, n_cur, n_hist,
  *                  n_heads, head_dim) bytes, 16-byte aligned: the codes and
  *                  scales (1 byte per Q/K element plus 4 bytes per scale).
- * Errors: those of ispa_attn_decomp, plus ISPA_ERR_WORKSPACE.
+ * Errors: those of ispa_attn_decomp, plus ISPA_ERR_WORKSPACE, and
+ *   ISPA_ERR_SHAPE when a segment has more than 2^31 64-key tiles x heads.
  */
 size_t ispa_attn_fp8_workspace_bytes(int64_t n_q, int64_t n_sink, int64_t n_cur,
                                      int64_t n_hist, int n_heads, int head_dim);

@@ -350,6 +350,10 @@ int ispa_attn_decomp_fp8(const void* q, int64_t n_q, const void* k_sink, const v
   if (st != ISPA_OK) return st;
   if (head_dim != 128) return ISPA_ERR_UNSUPPORTED;
   if (k_mean && !aligned16(k_mean)) return ISPA_ERR_ALIGN;
+  // one quantization workgroup per (64-key tile, head) and one per 4 query rows
+  for (const int64_t nk : {n_sink, n_cur, n_hist})
+    if (ispa::key_tiles(nk) * n_heads > INT32_MAX) return ISPA_ERR_SHAPE;
+  if ((n_q * n_heads + 3) / 4 > INT32_MAX) return ISPA_ERR_SHAPE;
   if (!run) return ISPA_OK;
   if (!workspace ||
       ws_bytes < ispa_attn_fp8_workspace_bytes(n_q, n_sink, n_cur, n_hist, n_heads, head_dim))
