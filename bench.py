@@ -582,11 +582,11 @@ def pmc_summary(fetch_csv: str, write_csv: str, w: wl.Workload):
     lines = [
         f"# HBM traffic per launch: attention and Gram kernels, {w.name}", "",
         "Commands (run from the repository root on one MI355X):", "", "```",
-        "cd /tmp && export TMPDIR=/tmp",
-        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o fetch -- {run}",
-        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o write -- {run}",
-        "python3 $REPO/bench.py --pmc-summary $REPO/gpurun_out/pmc_fetch/fetch_counter_collection.csv "
-        "$REPO/gpurun_out/pmc_write/write_counter_collection.csv",
+        "cd /tmp && export TMPDIR=/tmp    # REPO: the repository root; OUT: a results directory",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o fetch -- {run}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o write -- {run}",
+        "python3 $REPO/bench.py --pmc-summary $OUT/pmc_fetch/fetch_counter_collection.csv "
+        "$OUT/pmc_write/write_counter_collection.csv",
         "```", "",
         f"Calibration: the plain 1 GiB copy (the last large copy of the run) reads FETCH_SIZE = {fc:.0f} KiB "
         f"and WRITE_SIZE = {wc:.0f} KiB, so fetch counts are scaled by {f_fac:.4f} and write counts "
@@ -640,11 +640,11 @@ def pmc_mfma_summary(csv_path: str, w: wl.Workload):
     run = "python3 $REPO/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-stream"
     lines = [f"# Matrix-core counters per launch: attention and Gram kernels, {w.name}", "",
              "Commands (run from the repository root on one MI355X):", "", "```",
-             "cd /tmp && export TMPDIR=/tmp",
-             f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d $REPO/gpurun_out/pmc_mfma "
+             "cd /tmp && export TMPDIR=/tmp    # REPO: the repository root; OUT: a results directory",
+             f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d $OUT/pmc_mfma "
              f"-o mfma -- {run}",
              "python3 $REPO/bench.py --pmc-mfma-summary "
-             "$REPO/gpurun_out/pmc_mfma/mfma_counter_collection.csv", "```", "",
+             "$OUT/pmc_mfma/mfma_counter_collection.csv", "```", "",
              "| kernel | launches | matrix pipe busy | shader clock (GHz) | counted MFMA FLOP / "
              "algorithmic |", "|---|---:|---:|---:|---:|"]
     for name, ids, fl in rows:
@@ -677,8 +677,8 @@ def trace_table(trace_csv: str, command: str):
             agg[k] = (c + 1, t + int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     total = sum(t for _, t in agg.values())
     lines = ["Command (run from the repository root on one MI355X):", "", "```",
-             "cd /tmp && export TMPDIR=/tmp", command,
-             "python3 $REPO/bench.py --trace-table $REPO/gpurun_out/ktq/ktq_kernel_trace.csv",
+             "cd /tmp && export TMPDIR=/tmp    # REPO: the repository root; OUT: a results directory", command,
+             "python3 $REPO/bench.py --trace-table $OUT/ktq/ktq_kernel_trace.csv",
              "```", "", "| Kernel | Calls | Avg (us) | Total (ms) | % |",
              "|---|---:|---:|---:|---:|"]
     for k, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
@@ -713,10 +713,10 @@ def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
     lines = [
         f"# Kernel trace: {w.name}, {passes} steps (1 warmup + 1 timed)", "",
         "Command (run from the repository root on one MI355X):", "", "```",
-        "cd /tmp && export TMPDIR=/tmp",
-        "rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/kt -o kt -- "
+        "cd /tmp && export TMPDIR=/tmp    # REPO: the repository root; OUT: a results directory",
+        "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o kt -- "
         "python3 $REPO/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-stream",
-        f"python3 $REPO/bench.py --trace-summary $REPO/gpurun_out/kt/kt_kernel_trace.csv",
+        f"python3 $REPO/bench.py --trace-summary $OUT/kt/kt_kernel_trace.csv",
         "```", "",
         "| Kernel | Calls | Avg (us) | Total (ms) | % |", "|---|---:|---:|---:|---:|",
     ]
@@ -844,7 +844,7 @@ def main():
     if a.trace_table:
         sys.stdout.write(trace_table(
             a.trace_table, "rocprofv3 --kernel-trace --stats --output-format csv -d "
-            "$REPO/gpurun_out/ktq -o ktq -- python3 $REPO/bench.py --steps 1 --warmup 0 "
+            "$OUT/ktq -o ktq -- python3 $REPO/bench.py --steps 1 --warmup 0 "
             "--no-cpu-baseline"))
         return
     if a.trace_summary:
@@ -859,7 +859,7 @@ def main():
         return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: this library has no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 

@@ -1,5 +1,6 @@
 """Pins of the oracle's drift score (event-triggered recalibration, ISPA
-paper §3.3 last paragraph; the trigger itself is this build's reading).
+paper §3.3 last paragraph; the pages give no trigger, so the score is a
+reading of them).
 
 The score is the mean leverage x (G + lam I)^{-1} x^T of a chunk's local
 outputs over its warmup expectation tr((G + lam I)^{-1} G) / N. Pinned by
