@@ -179,3 +179,19 @@ def test_fp8_wan14_sampled_rows_and_heads():
            for k, v in gpu.items()}
     vmax = max(float(np.max(np.abs(a[:, heads]))) for a in (st.v_sink, st.v_cur, st.v_hist))
     check(sub, ref, delta, vmax)
+
+
+def test_fp8_wan13_layer_sampled_rows():
+    """1.3B-class layer (12 heads, 4680 queries, 1560 + 4680 local and 28080
+    history keys), smoothed by the oracle's key mean; 48 sampled query rows
+    of every head against the oracle."""
+    w = wl.WAN13_LAYER
+    st = wl.step_inputs(w, 0, 0)
+    log(f"fp8 attn {w.name}: n_q={st.q.shape[0]} hist={st.k_hist.shape[0]}")
+    mu = orc.bf16_round(orc.key_mean(st.k_sink, st.k_cur, st.k_hist))
+    gpu = run_fp8(st, w.sm_scale, mu)
+    rows = np.sort(np.random.default_rng(6).choice(st.q.shape[0], 48, replace=False))
+    ref, delta = oracle_fp8(st, w.sm_scale, mu, rows=rows)
+    sub = {k: (v[:, rows] if k.startswith("lse") else v[rows]) for k, v in gpu.items()}
+    vmax = max(float(np.max(np.abs(a))) for a in (st.v_sink, st.v_cur, st.v_hist))
+    check(sub, ref, delta, vmax)
