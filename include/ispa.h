@@ -207,8 +207,13 @@ int ispa_gram_accumulate(const void* x, const void* d, int64_t n_tok, int h,
  * Closed-form absorb (§3.2, §4.1): for each layer l,
  *   dW = argmin ||X (W + dW) - Z W||_F^2 + lambda ||dW||_F^2
  *      = (G + lambda I)^{-1} C W        (W = Wo^T, math layout [in, out]),
- * solved by a blocked fp32 Cholesky factorisation of G + lambda I and two
- * triangular solves. lambda is added unscaled to the summed statistics.
+ * computed as Y = (G + lambda I)^{-1} C by a blocked fp32 Cholesky
+ * factorisation of G + lambda I and two triangular solves, refined once with
+ * a residual C - (G + lambda I) Y accumulated in fp64 and solved with the same
+ * factor, then dW = Y W. The refinement keeps dW at the fp64 solution of the
+ * given fp32 statistics to ~1e-5 relative up to cond(G + lambda I) ~ 1e5
+ * (rank-deficient statistics have cond ~ ||G|| / lambda). lambda is added
+ * unscaled to the summed statistics.
  * G, C     [n_layers][h, h] fp32 (read only).
  * Wo       [n_layers][h, h] bf16, nn.Linear layout (read only).
  * dW       [n_layers][h, h] fp32 output, nn.Linear layout (like Wo).
@@ -231,7 +236,10 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C,
  * tokens:
  *   eps_abs = ||X (W + dW) - Z W||_F^2
  *           = tr(W^T E W) - tr(dW^T C W) - lambda ||dW||_F^2  (at the ridge
- *             optimum), Z = X + D,
+ *             optimum, which the refined solve of ispa_ridge_solve reaches
+ *             to fp32 rounding), Z = X + D, clamped at 0 (a near-exact fit
+ *             can come out below 0 by the fp32 rounding of the traces,
+ *             ~2^-24 sqrt(h) of ||Z W||^2),
  *   eps_rel = eps_abs / ||Z W||_F^2, ||Z W||^2 = tr(W^T (G + C + C^T + E) W);
  *   eps_rel = 0 when both are 0, +inf when only the denominator is 0.
  * Layers with info != 0 or a NaN error get +inf and are never selected.

@@ -184,7 +184,111 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(const GemmF32Para
   }
 }
 
+// Residual of the ridge system with fp64 accumulation, for one step of
+// iterative refinement of its fp32 solution (ISPA paper §3.2, closed-form
+// least squares; §4.1, ridge lambda):
+//   S[b] = C[b] - lambda Y[b] - G[b] Y[b]        (all h x h fp32, row-major)
+// The fp32 inputs are widened to fp64 on the way from LDS to the fp64 matrix
+// cores (v_mfma_f64_16x16x4f64), so each product is exact and the sum over k
+// is rounded at fp64 precision; only the small result is rounded to fp32.
+// The refinement needs this: the residual is a near-cancellation of C and
+// G Y, and an fp32-accumulated one carries errors of 2^-24 |G| |Y| that the
+// solve amplifies by up to 1/lambda.
+//
+// Tile 128 x 128 per workgroup, k-stage 16 (the fp32 tile loader above),
+// 4 waves of 64 x 64 = 4 x 4 blocks of 16 x 16. MFMA lane layout: lane l
+// holds A[m = l % 16][k = l / 16] and B[k = l / 16][n = l % 16]; result
+// register r of lane l is D[m = 4 r + l / 16][n = l % 16] (one row per
+// 64-bit register, the lane groups interleaved).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads, 2) void ridge_resid_f64_kernel(const RidgeResidParams p) {
+  __shared__ __attribute__((aligned(16))) float As[2][kTK * kLd];
+  __shared__ __attribute__((aligned(16))) float Bs[2][kTK * kLd];
+  const int h = p.h;
+  const int tiles_n = (h + kTN - 1) / kTN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  const int64_t b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, l16 = lane % 16, q = lane / 16;
+  const int wm = wave / 2, wn = wave % 2;
+  const float* G = p.G + b * hh;
+  const float* Y = p.Y + b * hh;
+
+  // A(m, k) = G[m][k] (k contiguous); B(k, n) = Y[k][n] (n contiguous)
+  TileLoader<true, false> la;
+  TileLoader<false, false> lb;
+  f64x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  const int nk = (h + kTK - 1) / kTK;
+  la.load(G, h, 1, tm * kTM, h, 0, h, tid);
+  lb.load(Y, 1, h, tn * kTN, h, 0, h, tid);
+  la.store(As[0], tid);
+  lb.store(Bs[0], tid);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    const bool has_next = ks + 1 < nk;
+    if (has_next) {
+      la.load(G, h, 1, tm * kTM, h, (ks + 1) * kTK, h, tid);
+      lb.load(Y, 1, h, tn * kTN, h, (ks + 1) * kTK, h, tid);
+    }
+    const float* as = As[buf];
+    const float* bs = Bs[buf];
+#pragma unroll
+    for (int kk = 0; kk < kTK / 4; ++kk) {
+      const int k = 4 * kk + q;
+      double a[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = static_cast<double>(as[k * kLd + wm * 64 + i * 16 + l16]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = static_cast<double>(bs[k * kLd + wn * 64 + j * 16 + l16]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    if (has_next) {
+      la.store(As[buf ^ 1], tid);
+      lb.store(Bs[buf ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  const float* C = p.C + b * hh;
+  float* S = p.S + b * hh;
+  const double lam = p.lam;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = tn * kTN + wn * 64 + j * 16 + l16;
+      if (n >= h) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = tm * kTM + wm * 64 + i * 16 + 4 * r + q;
+        if (m >= h) continue;
+        const int64_t e = static_cast<int64_t>(m) * h + n;
+        const double v = static_cast<double>(C[e]) - lam * static_cast<double>(Y[e]) - acc[i][j][r];
+        S[e] = static_cast<float>(v);
+      }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ridge_resid_f64(const RidgeResidParams& p, hipStream_t stream) {
+  if (p.h <= 0 || p.batch <= 0) return hipSuccess;
+  const int t = (p.h + kTM - 1) / kTM;
+  hipLaunchKernelGGL(ridge_resid_f64_kernel, dim3(t * t, p.batch), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_f32(const GemmF32Params& p, hipStream_t stream) {
   if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;

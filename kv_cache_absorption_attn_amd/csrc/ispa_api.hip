@@ -28,7 +28,8 @@ size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct RidgeWs {
   float* L;       // [n_layers][h, h] Cholesky factor (later: W W^T for scoring)
-  float* R;       // [n_layers][h, h] right-hand side -> dW (math layout)
+  float* R;       // [n_layers][h, h] right-hand side -> (G + lambda I)^-1 C
+  float* S;       // [n_layers][h, h] refinement residual / correction, staging
   float* Bt;      // [n_layers][h, h] (C W)^T in nn.Linear layout
   float* Linv;    // [n_layers][h, 128] inverses of the diagonal blocks
   double* part;   // layer-score partial sums
@@ -44,6 +45,7 @@ RidgeWs ridge_layout(void* base, int n_layers, int h) {
   size_t off = 0;
   w.L = reinterpret_cast<float*>(p + off);    off = align_up(off + hh);
   w.R = reinterpret_cast<float*>(p + off);    off = align_up(off + hh);
+  w.S = reinterpret_cast<float*>(p + off);    off = align_up(off + hh);
   w.Bt = reinterpret_cast<float*>(p + off);   off = align_up(off + hh);
   w.Linv = reinterpret_cast<float*>(p + off); off = align_up(off + lin);
   w.part = reinterpret_cast<double*>(p + off); off = align_up(off + part);
@@ -68,50 +70,51 @@ hipError_t gemm(int M, int N, int K, const void* A, int64_t a_s0, int64_t a_s1, 
 // Block rows [ba, bb) of R (128 rows per block, the last one possibly short).
 inline int blk_row(int b, int h) { return b * kCholBlock < h ? b * kCholBlock : h; }
 
-// R[rows of blocks ba..bb) <- L^-1 R for the lower-triangular factor in w.L.
-hipError_t solve_lower(int ba, int bb, const RidgeWs& w, int h, int L, hipStream_t s) {
+// R[rows of blocks ba..bb) <- L^-1 R for the lower-triangular factor in w.L
+// (R: h x h right-hand sides of each layer, overwritten by the solution).
+hipError_t solve_lower(int ba, int bb, const RidgeWs& w, float* R, int h, int L, hipStream_t s) {
   const int64_t hh = static_cast<int64_t>(h) * h;
   const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
   const int r0 = blk_row(ba, h), r2 = blk_row(bb, h);
   if (bb - ba == 1) {
-    float* rk = w.R + static_cast<int64_t>(r0) * h;
+    float* rk = R + static_cast<int64_t>(r0) * h;
     const float* linv = w.Linv + static_cast<int64_t>(r0) * kCholBlock;
     const int nbk = r2 - r0;
     return gemm(nbk, h, nbk, linv, kCholBlock, 1, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
                 0.f, L, false, s);
   }
   const int bm = (ba + bb) / 2, r1 = blk_row(bm, h);
-  hipError_t e = solve_lower(ba, bm, w, h, L, s);
+  hipError_t e = solve_lower(ba, bm, w, R, h, L, s);
   if (e != hipSuccess) return e;
   // R[r1:r2] -= L[r1:r2, r0:r1] R[r0:r1]
   e = gemm(r2 - r1, h, r1 - r0, w.L + static_cast<int64_t>(r1) * h + r0, h, 1, hh, false,
-           w.R + static_cast<int64_t>(r0) * h, h, 1, hh, false, w.R + static_cast<int64_t>(r1) * h,
+           R + static_cast<int64_t>(r0) * h, h, 1, hh, false, R + static_cast<int64_t>(r1) * h,
            h, hh, -1.f, 1.f, L, false, s);
   if (e != hipSuccess) return e;
-  return solve_lower(bm, bb, w, h, L, s);
+  return solve_lower(bm, bb, w, R, h, L, s);
 }
 
 // R[rows of blocks ba..bb) <- L^-T R.
-hipError_t solve_upper(int ba, int bb, const RidgeWs& w, int h, int L, hipStream_t s) {
+hipError_t solve_upper(int ba, int bb, const RidgeWs& w, float* R, int h, int L, hipStream_t s) {
   const int64_t hh = static_cast<int64_t>(h) * h;
   const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
   const int r0 = blk_row(ba, h), r2 = blk_row(bb, h);
   if (bb - ba == 1) {
-    float* rk = w.R + static_cast<int64_t>(r0) * h;
+    float* rk = R + static_cast<int64_t>(r0) * h;
     const float* linv = w.Linv + static_cast<int64_t>(r0) * kCholBlock;
     const int nbk = r2 - r0;
     return gemm(nbk, h, nbk, linv, 1, kCholBlock, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
                 0.f, L, false, s);
   }
   const int bm = (ba + bb) / 2, r1 = blk_row(bm, h);
-  hipError_t e = solve_upper(bm, bb, w, h, L, s);
+  hipError_t e = solve_upper(bm, bb, w, R, h, L, s);
   if (e != hipSuccess) return e;
   // R[r0:r1] -= L[r1:r2, r0:r1]^T R[r1:r2]
   e = gemm(r1 - r0, h, r2 - r1, w.L + static_cast<int64_t>(r1) * h + r0, 1, h, hh, false,
-           w.R + static_cast<int64_t>(r1) * h, h, 1, hh, false, w.R + static_cast<int64_t>(r0) * h,
+           R + static_cast<int64_t>(r1) * h, h, 1, hh, false, R + static_cast<int64_t>(r0) * h,
            h, hh, -1.f, 1.f, L, false, s);
   if (e != hipSuccess) return e;
-  return solve_upper(ba, bm, w, h, L, s);
+  return solve_upper(ba, bm, w, R, h, L, s);
 }
 
 // Columns of blocks [ca, cb) of the rows [x0, x1) of w.L: X <- X L^-T for the
@@ -447,7 +450,6 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const 
   const hipStream_t s = as_stream(stream);
   const RidgeWs w = ridge_layout(workspace, n_layers, h);
   const int64_t hh = static_cast<int64_t>(h) * h;
-  const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
   const int L = n_layers;
   const int nblk = (h + kCholBlock - 1) / kCholBlock;
 
@@ -458,11 +460,56 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const 
   ISPA_TRY(ispa::launch_copy_add_diag(G, w.L, h, L, lambda, s));
   ISPA_TRY(cholesky(0, nblk, w, h, L, info, s));
 
-  // R = C W (math layout [in, out]); W(k, o) = Wo[o][k], i.e. R[i][o] =
-  // sum_k C[i][k] Wo[o][k]: on the bf16 matrix cores with C split into two
-  // bf16 planes (hi + lo holds C to ~2^-17 relative, about the rounding of an
-  // fp32 accumulation over k), staged in Bt, which is free until (C W)^T is
-  // written there below. Keep (C W)^T for scoring.
+  // Y0 = (G + lambda I)^-1 C by forward substitution L Z = C and back
+  // substitution L^T Y0 = Z, both by recursive halving over the 128-row
+  // blocks: solve one half, update the other half with one large GEMM (K up
+  // to h/2), solve it. The leaves apply the diagonal-block inverses in place.
+  // Compared with block-row sweeps this touches each row of the right-hand
+  // side O(log(h/128)) times instead of O(h/128) times, and the update GEMMs
+  // are large.
+  ISPA_TRY(hipMemcpyAsync(w.R, C, static_cast<size_t>(L) * hh * sizeof(float),
+                          hipMemcpyDeviceToDevice, s));
+  ISPA_TRY(solve_lower(0, nblk, w, w.R, h, L, s));
+  ISPA_TRY(solve_upper(0, nblk, w, w.R, h, L, s));
+
+  // One step of iterative refinement: the residual S = C - (G + lambda I) Y0
+  // accumulated in fp64, the correction (G + lambda I)^-1 S from the same
+  // factor, Y = Y0 + correction. The fp32 factor solves to about cond * 2^-24
+  // (1e-3 relative at cond 2e4, rank-deficient statistics: eigenvalues lambda
+  // outside the span of the warmup tokens); with the fp64 residual one step
+  // brings that to about (cond * 2^-24)^2. The system is solved for
+  // (G + lambda I)^-1 C rather than for dW directly, so that its right-hand
+  // side C is an exact input: C W formed in fp32 would carry a rounding of
+  // 2^-24 |C| |W| that no refinement of the solve can remove, and the
+  // multiplication by W after the solve is well conditioned.
+  {
+    ispa::RidgeResidParams rp{};
+    rp.h = h;
+    rp.batch = L;
+    rp.G = G;
+    rp.C = C;
+    rp.Y = w.R;
+    rp.S = w.S;
+    rp.lam = static_cast<double>(lambda);
+    ISPA_TRY(ispa::launch_ridge_resid_f64(rp, s));
+  }
+  ISPA_TRY(solve_lower(0, nblk, w, w.S, h, L, s));
+  ISPA_TRY(solve_upper(0, nblk, w, w.S, h, L, s));
+  ISPA_TRY(ispa::launch_add_inplace(w.R, w.S, static_cast<int64_t>(L) * hh, s));
+
+  // dW (math layout [in, out]) = Y W, W(k, o) = Wo[o][k]: dW[i][o] =
+  // sum_k Y[i][k] Wo[o][k] on the bf16 matrix cores with Y split into two
+  // bf16 planes (hi + lo holds Y to ~2^-17 relative per element; the errors
+  // are independent and stay at that level in the product), staged in Bt;
+  // then the transpose into the caller's nn.Linear layout.
+  {
+    uint16_t* yhi = reinterpret_cast<uint16_t*>(w.Bt);
+    uint16_t* ylo = yhi + static_cast<int64_t>(L) * hh;
+    ISPA_TRY(ispa::launch_split_nt_gemm_f32(w.R, yhi, ylo, static_cast<const uint16_t*>(Wo), w.S,
+                                            h, L, s));
+  }
+  ISPA_TRY(ispa::launch_transpose(w.S, dW, h, L, s));
+  // (C W)^T in nn.Linear layout for the layer score, the same way.
   {
     uint16_t* chi = reinterpret_cast<uint16_t*>(w.Bt);
     uint16_t* clo = chi + static_cast<int64_t>(L) * hh;
@@ -470,16 +517,6 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const 
                                             L, s));
   }
   ISPA_TRY(ispa::launch_transpose(w.R, w.Bt, h, L, s));
-
-  // Forward substitution L Z = R, then back substitution L^T X = Z, both by
-  // recursive halving over the 128-row blocks: solve one half, update the
-  // other half with one large GEMM (K up to h/2), solve it. The leaves apply
-  // the diagonal-block inverses in place. Compared with block-row sweeps this
-  // touches each row of R O(log(h/128)) times instead of O(h/128) times, and
-  // the update GEMMs are large.
-  ISPA_TRY(solve_lower(0, nblk, w, h, L, s));
-  ISPA_TRY(solve_upper(0, nblk, w, h, L, s));
-  ISPA_TRY(ispa::launch_transpose(w.R, dW, h, L, s));
   return ISPA_OK;
 }
 
@@ -569,7 +606,7 @@ int ispa_drift_prepare(int n_layers, int h, const float* G, float lambda, int64_
   ISPA_TRY(ispa::launch_copy_add_diag(G, w.L, h, n_layers, lambda, s));
   ISPA_TRY(cholesky(0, nblk, w, h, n_layers, info, s));
   ISPA_TRY(ispa::launch_identity(linv, h, n_layers, s));
-  ISPA_TRY(solve_lower(0, nblk, w, h, n_layers, s));
+  ISPA_TRY(solve_lower(0, nblk, w, w.R, h, n_layers, s));
   // ||L^{-1}||_F^2 = tr((G + lambda I)^{-1}) -> (h - lambda tr) / n_warm
   ISPA_TRY(ispa::launch_drift_sum(linv, h, h, h, hh, n_layers, w.part, h, lambda,
                                   static_cast<double>(n_warm), nullptr, ref, s));

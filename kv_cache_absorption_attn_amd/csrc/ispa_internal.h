@@ -105,6 +105,20 @@ struct GemmF32Params {
 };
 hipError_t launch_gemm_f32(const GemmF32Params& p, hipStream_t stream);
 
+// S[b] = C[b] - lam Y[b] - G[b] Y[b] for h x h fp32 row-major matrices, the
+// products and the sum in fp64 (the residual of one refinement step).
+struct RidgeResidParams {
+  int h, batch;
+  const float* G;
+  const float* C;
+  const float* Y;
+  float* S;
+  double lam;
+};
+hipError_t launch_ridge_resid_f64(const RidgeResidParams& p, hipStream_t stream);
+// y[i] += x[i] over n fp32 elements (n % 4 == 0, 16-byte aligned).
+hipError_t launch_add_inplace(float* y, const float* x, int64_t n, hipStream_t stream);
+
 // ---------------------------------------------------------------- ridge pieces
 hipError_t launch_copy_add_diag(const float* G, float* L, int h, int batch, float lam,
                                 hipStream_t stream);

@@ -123,6 +123,18 @@ __global__ __launch_bounds__(256) void potrf_block_kernel(float* __restrict__ L,
   }
 }
 
+// y += x elementwise (float4; the refinement's Y = Y0 + correction).
+__global__ void add_inplace_kernel(float* __restrict__ y, const float* __restrict__ x,
+                                   int64_t n4) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float4 a = reinterpret_cast<float4*>(y)[i];
+    const float4 b = reinterpret_cast<const float4*>(x)[i];
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    reinterpret_cast<float4*>(y)[i] = a;
+  }
+}
+
 // dst[b](j, i) = src[b](i, j) for an h x h matrix, 32 x 32 tiles via LDS.
 __global__ void transpose_kernel(const float* __restrict__ src, float* __restrict__ dst, int h) {
   __shared__ float t[32][33];
@@ -202,6 +214,12 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(const ScoreParams p,
 // eps_abs = tr(W^T E W) - tr(dW^T C W) - lambda ||dW||^2
 // eps_rel = eps_abs / ||Z W||^2,  ||Z W||^2 = tr(W^T (G + C + C^T + E) W)
 // then a stable ascending ranking; the first K valid layers are selected.
+// The first form equals the direct residual ||X (W + dW) - Z W||^2 at the
+// ridge optimum; away from it the two differ by tr(dW^T r) with r = C W -
+// (G + lambda I) dW, which the refined solve keeps at the level of fp32
+// rounding. What remains is the rounding of the fp32 traces, of the order
+// of 2^-24 sqrt(h) of ||Z W||^2; a near-exact fit can fall below zero by
+// that much, and a squared norm is clamped at zero.
 __global__ __launch_bounds__(256) void score_finalize_kernel(const ScoreParams p, int nrb) {
   extern __shared__ double key[];
   const int L = p.n_layers;
@@ -211,6 +229,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(const ScoreParams p
       for (int q = 0; q < kNPart; ++q) s[q] += p.partial[(static_cast<int64_t>(l) * nrb + rb) * kNPart + q];
     const double tew = s[0], tgw = s[1], tcw = s[2], tdb = s[3], dd = s[4];
     double ea = tew - tdb - static_cast<double>(p.lam) * dd;
+    if (ea < 0.0) ea = 0.0;
     const double den = tgw + 2.0 * tcw + tew;
     double er = den > 0.0 ? ea / den : (ea == 0.0 ? 0.0 : INFINITY);
     const bool bad = (p.info && p.info[l] != 0) || isnan(ea) || isnan(er);
@@ -357,6 +376,15 @@ hipError_t launch_potrf_block(float* L, float* Linv, int h, int k0, int nb, int 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(potrf_block_kernel, dim3(batch), dim3(256), lds, stream, L, Linv, h, k0, nb,
                      info, info_first);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_inplace(float* y, const float* x, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = (n4 + 255) / 256;
+  hipLaunchKernelGGL(add_inplace_kernel, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)),
+                     dim3(256), 0, stream, y, x, n4);
   return hipGetLastError();
 }
 
