@@ -47,7 +47,9 @@ enum {
   ISPA_ERR_UNSUPPORTED = 3, /* a valid but unsupported configuration */
   ISPA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ISPA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
-  ISPA_ERR_HIP = 6          /* the HIP runtime reported an error (launch, copy, mapping) */
+  ISPA_ERR_HIP = 6,         /* the HIP runtime reported an error (launch, copy, mapping) */
+  ISPA_ERR_SCRATCH = 7      /* input too large for an allocation-free entry point's
+                               fixed scratch */
 };
 
 /* Static text for a status code (never NULL). */
@@ -327,6 +329,30 @@ size_t ispa_project_w8a8_workspace_bytes(int64_t n, int h_in);
 int ispa_project_w8a8(const void* x, const void* wq, const float* w_scale, void* y,
                       int64_t n, int h_in, int h_out, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/*
+ * Allocation-free W8A8 projection, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): ispa_project_w8a8 without the workspace argument. The
+ * quantized tokens are staged in a fixed scratch array of the library
+ * (ISPA_NOALLOC_MAX_CODE_BYTES of codes plus ISPA_NOALLOC_MAX_TOKENS fp32
+ * scales, 32.25 MiB), of which each GPU the library runs on holds its own
+ * copy until the process ends. The call allocates nothing: on its first
+ * call on a device (with that device current) it looks up that device's copy
+ * with hipGetSymbolAddress, once. The caller passes inputs and outputs as
+ * for ispa_project_w8a8 and gets the same result, bit for bit.
+ * Calls on one GPU share its scratch: calls that overlap on one GPU (on
+ * different streams, or from host threads without ordering between them)
+ * race and must be serialised by the caller.
+ * Errors: those of ispa_project_w8a8 (no ISPA_ERR_WORKSPACE), plus
+ *   ISPA_ERR_SCRATCH when n > ISPA_NOALLOC_MAX_TOKENS or n * h_in >
+ *   ISPA_NOALLOC_MAX_CODE_BYTES, and ISPA_ERR_HIP when the scratch address
+ *   cannot be looked up.
+ */
+#define ISPA_NOALLOC_MAX_CODE_BYTES (32 * 1024 * 1024)
+#define ISPA_NOALLOC_MAX_TOKENS 65536
+int ispa_project_w8a8_noalloc(const void* x, const void* wq, const float* w_scale, void* y,
+                              int64_t n, int h_in, int h_out, void* stream);
 
 /*
  * Drift score for event-triggered recalibration (§3.3, last paragraph: on a

@@ -24,6 +24,9 @@ ISPA_ERR_UNSUPPORTED = 3
 ISPA_ERR_ALIGN = 4
 ISPA_ERR_WORKSPACE = 5
 ISPA_ERR_HIP = 6
+ISPA_ERR_SCRATCH = 7
+NOALLOC_MAX_CODE_BYTES = 32 * 1024 * 1024
+NOALLOC_MAX_TOKENS = 65536
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -120,6 +123,8 @@ lib.ispa_project_w8a8_workspace_bytes.restype = _sz
 lib.ispa_project_w8a8_workspace_bytes.argtypes = [_i64, _i]
 lib.ispa_project_w8a8.restype = _i
 lib.ispa_project_w8a8.argtypes = [_p, _p, _p, _p, _i64, _i, _i, _p, _sz, _p]
+lib.ispa_project_w8a8_noalloc.restype = _i
+lib.ispa_project_w8a8_noalloc.argtypes = [_p, _p, _p, _p, _i64, _i, _i, _p]
 lib.ispa_kv_restore_history.restype = _i
 lib.ispa_kv_restore_history.argtypes = [_p, _i]
 lib.ispa_drift_workspace_bytes.restype = _sz
@@ -192,7 +197,7 @@ EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram
             "ispa_quantize_fp8", "ispa_project_w8a8_workspace_bytes", "ispa_project_w8a8",
             "ispa_attn_fp8_workspace_bytes", "ispa_attn_decomp_fp8",
             "ispa_key_mean_workspace_bytes", "ispa_key_mean", "ispa_attn_decomp_grouped",
-            "ispa_project_grouped", "ispa_session_layer_grouped")
+            "ispa_project_grouped", "ispa_session_layer_grouped", "ispa_project_w8a8_noalloc")
 
 
 class IspaError(RuntimeError):
@@ -686,6 +691,22 @@ def ispa_project_w8a8(x, wq, w_scale, y, workspace, *, stream=None) -> None:
                                _ptr(workspace, None, "workspace"),
                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ispa_project_w8a8", st)
+
+
+def ispa_project_w8a8_noalloc(x, wq, w_scale, y, *, stream=None) -> None:
+    """ispa_project_w8a8 with the quantized tokens staged in the library's
+    fixed per-device scratch instead of a workspace: allocates nothing. At most
+    NOALLOC_MAX_TOKENS rows and NOALLOC_MAX_CODE_BYTES bytes of codes (n * h_in);
+    calls that overlap on one GPU race on its scratch."""
+    n, h_in = x.shape
+    h_out = wq.shape[0]
+    if wq.shape[1] != h_in or tuple(w_scale.shape) != (h_out,) or tuple(y.shape) != (n, h_out):
+        raise ValueError("ispa_project_w8a8_noalloc: shape mismatch")
+    st = lib.ispa_project_w8a8_noalloc(_ptr(x, torch.bfloat16, "x"), _ptr(wq, torch.uint8, "wq"),
+                                       _ptr(w_scale, torch.float32, "w_scale"),
+                                       _ptr(y, torch.bfloat16, "y"), n, h_in, h_out,
+                                       _stream(stream))
+    _check("ispa_project_w8a8_noalloc", st)
 
 
 def ispa_session_layer_grouped(sessions, layer: int, qs, ys, *, stream=None) -> None:

@@ -177,6 +177,7 @@ const char* ispa_status_string(int status) {
     case ISPA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case ISPA_ERR_WORKSPACE: return "workspace missing or too small";
     case ISPA_ERR_HIP: return "HIP runtime error (launch, copy or memory mapping)";
+    case ISPA_ERR_SCRATCH: return "input exceeds the fixed scratch of an allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings():
     assert ispa.ispa_status_string(0) == "ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert ispa.ispa_status_string(s) not in ("ok", "unknown status")
     assert ispa.ispa_status_string(99) == "unknown status"
     assert ispa.ispa_version() >= 100
@@ -210,6 +210,18 @@ def test_w8a8_validation():
     assert pw(A, A, A, A, 100, 256, 128, 0, need, 0) == WS
     assert pw(A, A, A, MIS, 100, 256, 128, A, need, 0) == ALIGN
     assert pw(A, A, A, A, 0, 256, 128, 0, 0, 0) == OK
+    # the allocation-free variant: the same checks, and sizes beyond its
+    # fixed scratch, all before it looks up its scratch on a device
+    na = _lib.lib.ispa_project_w8a8_noalloc
+    assert na(A, A, 0, A, 100, 256, 128, 0) == NULL
+    assert na(A, A, A, A, -1, 256, 128, 0) == SHAPE
+    assert na(A, A, A, A, 100, 96, 128, 0) == UNSUP
+    assert na(A, A, A, A, 100, 256, 100, 0) == UNSUP
+    assert na(A, A, A, A, _lib.NOALLOC_MAX_TOKENS + 1, 64, 128, 0) == _lib.ISPA_ERR_SCRATCH
+    rows = _lib.NOALLOC_MAX_CODE_BYTES // 5120 + 1
+    assert na(A, A, A, A, rows, 5120, 128, 0) == _lib.ISPA_ERR_SCRATCH
+    assert na(A, A, A, MIS, 100, 256, 128, 0) == ALIGN
+    assert na(A, A, A, A, 0, 256, 128, 0) == OK
 
 
 def test_kv_cache_validation():
