@@ -3,12 +3,12 @@
 
 One step = the whole warmup-to-absorption pass of the 14B-class workload:
 for each of 4 warmup chunks (history 0 -> 36 latent frames) and each of the
-40 layers, the decomposable attention (O_full, X = O_local, D, the last two kept
-resident for all warmup chunks); then per layer the Gram statistics over all
-its warmup tokens in one call; then, batched over the 40 layers, the ridge
-solve for dW, the
-layer errors, the selection of K = 20 layers and the in-place bf16 update of
-their output projections. All inputs are resident in HBM before timing
+40 layers, the decomposable attention (O_full token-major for the model;
+X = O_local and D feature-major, kept resident for all warmup chunks); then
+the Gram statistics of all 40 layers over all their warmup tokens in one
+call; then, batched over the 40 layers, the ridge solve for dW, the layer
+errors, the selection of K = 20 layers and the in-place bf16 update of their
+output projections. All inputs are resident in HBM before timing
 starts; W_o is restored from a pristine copy at the start of every step.
 
 Prints one JSON line. `value` is the decomposable-attention throughput in
@@ -46,8 +46,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_gram_wan14b_warmup_hbm_traff
 KERNEL_SOURCES = {
     "attn_decomp_kernel<128, false>": ["kv_cache_absorption_attn_amd/csrc/attn_decomp.hip",
                                        "kv_cache_absorption_attn_amd/csrc/device_common.h"],
-    "gram_kernel": ["kv_cache_absorption_attn_amd/csrc/gram.hip",
-                    "kv_cache_absorption_attn_amd/csrc/device_common.h"],
+    "gram_t_kernel": ["kv_cache_absorption_attn_amd/csrc/gemm256.hip",
+                      "kv_cache_absorption_attn_amd/csrc/device_common.h",
+                      "kv_cache_absorption_attn_amd/csrc/lds_dma_asm.h"],
 }
 COPY_BYTES = 1 << 30
 
@@ -98,11 +99,11 @@ class Inputs:
         # outputs / state
         self.o_full = torch.empty(w.n_q, h, dtype=bf, device=dev)
         self.x = torch.empty(w.n_q, h, dtype=bf, device=dev)
-        # every warmup step's X and D stay resident until the transition
-        # (2 x T_warm x N x h bf16 per layer: 15.3 GB at 14B)
-        self.xs = [torch.empty(w.n_steps * w.n_q, h, dtype=bf, device=dev)
-                   for _ in range(w.n_layers)]
-        self.ds = [torch.empty_like(self.xs[0]) for _ in range(w.n_layers)]
+        # every warmup step's X and D stay resident until the transition,
+        # feature-major (token-contiguous per feature), the warmup steps of a
+        # layer side by side: [L, h, T_warm * N] bf16, 15.3 GB for both at 14B
+        self.xt = torch.empty(w.n_layers, h, w.n_steps * w.n_q, dtype=bf, device=dev)
+        self.dt = torch.empty_like(self.xt)
         self.y = torch.empty(w.n_q, h, dtype=bf, device=dev)
         f32 = torch.float32
         self.G = torch.empty(w.n_layers, h, h, dtype=f32, device=dev)
@@ -139,18 +140,17 @@ def run_step(ispa, inp: Inputs, ws, timing: dict | None):
         for l in range(w.n_layers):
             kh, vh = inp.hist_view(l, s)
             mark("attn0")
-            ispa.ispa_attn_decomp(inp.q[l][s], inp.k_sink[l], inp.v_sink[l], inp.k_cur[l][s],
-                                  inp.v_cur[l][s], kh, vh, w.sm_scale,
-                                  o_local=inp.xs[l][s * n:(s + 1) * n], o_full=inp.o_full,
-                                  d_out=inp.ds[l][s * n:(s + 1) * n])
+            ispa.ispa_attn_decomp_t(inp.q[l][s], inp.k_sink[l], inp.v_sink[l],
+                                    inp.k_cur[l][s], inp.v_cur[l][s], kh, vh, w.sm_scale,
+                                    inp.xt[l], inp.dt[l], col=s * n, o_full=inp.o_full)
             mark("attn1")
-    # the warmup statistics of each layer in one call over all its warmup
-    # tokens (the per-call cost is paid once per layer, not once per step)
-    for l in range(w.n_layers):
-        mark("gram0")
-        ispa.ispa_gram_accumulate(inp.xs[l], inp.ds[l], inp.G[l], inp.C[l], inp.E[l],
-                                  zero_first=True)
-        mark("gram1")
+    # the warmup statistics of every layer in one call over all warmup tokens
+    # (the per-call cost is paid once, and the 40 layers' tiles fill the chip
+    # with no partial last round)
+    mark("gram0")
+    ispa.ispa_gram_accumulate_t(inp.xt, inp.dt, w.n_steps * n, inp.G, inp.C, inp.E,
+                                zero_first=True)
+    mark("gram1")
     mark("absorb0")
     ispa.ispa_ridge_solve(inp.G, inp.C, inp.wo, w.lam, inp.dW, inp.info, ws)
     mark("ridge1")
@@ -475,11 +475,13 @@ def multi_instance_measure(ispa, w: wl.Workload, n_inst: int = 8, n_q: int = 512
 
 
 def gram_deferred_measure(ispa, w: wl.Workload, reps: int = 5, seed: int = 5):
-    """One layer's warmup statistics two ways: one Gram call per warmup step
-    (N tokens each, as the warmup pass runs it) against a single call over
-    all T_warm steps' X and D kept resident (T_warm * N tokens), which pays
-    the per-call cost (pipeline fill, tile write-out, fp32 read-modify-write
-    of G, C, E) once. Same sums; HIP events on the launch stream."""
+    """One layer's warmup statistics three ways: one token-major Gram call
+    per warmup step (N tokens each), a single token-major call over all
+    T_warm steps' X and D kept resident (T_warm * N tokens), which pays the
+    per-call cost (pipeline fill, tile write-out, fp32 read-modify-write of
+    G, C, E) once, and the single feature-major call the warmup pass makes
+    (ispa_gram_accumulate_t, here for one layer). Same sums; HIP events on
+    the launch stream."""
     dev, bf = "cuda", torch.bfloat16
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
@@ -496,6 +498,11 @@ def gram_deferred_measure(ispa, w: wl.Workload, reps: int = 5, seed: int = 5):
     def once():
         ispa.ispa_gram_accumulate(x, d, G, C, E, zero_first=True)
 
+    xt, dt = x.t().contiguous(), d.t().contiguous()
+
+    def once_t():
+        ispa.ispa_gram_accumulate_t(xt, dt, T * n, G, C, E, zero_first=True)
+
     def timed(fn):
         fn()
         torch.cuda.synchronize()
@@ -507,11 +514,13 @@ def gram_deferred_measure(ispa, w: wl.Workload, reps: int = 5, seed: int = 5):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    t_step, t_once = timed(per_step), timed(once)
+    t_step, t_once, t_once_t = timed(per_step), timed(once), timed(once_t)
     fl = gram_flops(T * n, h)
     return {"tokens": T * n, "per_step_calls_ms": round(t_step, 3),
             "one_call_ms": round(t_once, 3), "per_step_tflops": round(fl / t_step / 1e9, 1),
             "one_call_tflops": round(fl / t_once / 1e9, 1),
+            "feature_major_one_call_ms": round(t_once_t, 3),
+            "feature_major_one_call_tflops": round(fl / t_once_t / 1e9, 1),
             "resident_activation_gb_per_layer": round(2 * T * n * h * 2 / 1e9, 3)}
 
 
@@ -567,12 +576,11 @@ def pmc_summary(fetch_csv: str, write_csv: str, w: wl.Workload):
         copy = [v for _, n, v in rows if "copyBuffer" in n and v > 1024][-1]
         attn = [v for _, n, v in rows if "attn_decomp_kernel<128, false>" in n]
         attn = [v for i, v in enumerate(attn) if i % (n_warm + n_post) < n_warm]
-        # each step: one warmup Gram launch per layer (over all its warmup
-        # tokens), then one G-only launch (W_o^T W_o of the layer score),
-        # which is left out
-        gram = [v for _, n, v in rows if "gram_kernel" in n]
-        gram = [v for i, v in enumerate(gram) if i % (w.n_layers + 1) < w.n_layers]
-        return copy, {"attn_decomp_kernel<128, false>": attn, "gram_kernel": gram}
+        # each step: one feature-major Gram launch over every layer and all
+        # warmup tokens (the G-only W_o^T W_o of the layer score is another
+        # kernel)
+        gram = [v for _, n, v in rows if "gram_t_kernel" in n]
+        return copy, {"attn_decomp_kernel<128, false>": attn, "gram_t_kernel": gram}
 
     fc, fe = read(fetch_csv, "FETCH_SIZE")
     wc, wr = read(write_csv, "WRITE_SIZE")
@@ -632,11 +640,10 @@ def pmc_mfma_summary(csv_path: str, w: wl.Workload):
     n_kv = [w.n_sink + w.n_cur + hs for hs in w.hist_per_step]
     attn_ids = sorted(i for i, n in names.items() if "attn_decomp_kernel<128, false>" in n)
     attn_ids = [i for j, i in enumerate(attn_ids) if j % (n_warm + n_post) < n_warm]
-    gram_ids = sorted(i for i, n in names.items() if "gram_kernel" in n)
-    gram_ids = [i for j, i in enumerate(gram_ids) if j % (w.n_layers + 1) < w.n_layers]
+    gram_ids = sorted(i for i, n in names.items() if "gram_t_kernel" in n)
     rows = [("attn_decomp_kernel<128, false>", attn_ids,
              sum(attn_flops(w.n_q, nk, w.hidden) for nk in n_kv) / len(n_kv)),
-            ("gram_kernel", gram_ids, gram_flops(w.n_steps * w.n_q, w.hidden))]
+            ("gram_t_kernel", gram_ids, gram_flops(w.n_steps * w.n_q, w.hidden) * w.n_layers)]
     run = "python3 $REPO/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-stream"
     lines = [f"# Matrix-core counters per launch: attention and Gram kernels, {w.name}", "",
              "Commands (run from the repository root on one MI355X):", "", "```",
@@ -706,8 +713,7 @@ def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
     attn = [dt for _, n, dt in rows if "attn_decomp_kernel<128, false>" in n]
     warm = [dt for i, dt in enumerate(attn) if i % (n_warm + n_post) < n_warm]
     post = [dt for i, dt in enumerate(attn) if i % (n_warm + n_post) >= n_warm]
-    gram = [dt for _, n, dt in rows if "gram_kernel" in n]
-    gram = [dt for i, dt in enumerate(gram) if i % (w.n_layers + 1) < w.n_layers]  # warmup only
+    gram = [dt for _, n, dt in rows if "gram_t_kernel" in n]
     n_kv = [w.n_sink + w.n_cur + hs for hs in w.hist_per_step]
     fl = sum(attn_flops(w.n_q, nk, w.hidden) for nk in n_kv) / len(n_kv)
     lines = [
@@ -735,22 +741,25 @@ def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
                      f"full only): {len(post)}, average {sum(post) / len(post) / 1e3:.1f} us.")
     if gram:
         avg = sum(gram) / len(gram)
-        gf = gram_flops(w.n_steps * w.n_q, w.hidden)
-        lines.append(f"Gram launches: {len(gram)}, average {avg / 1e3:.1f} us for "
-                     f"{gf / 1e9:.1f} GFLOP = {gf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
-    proj = [dt for _, n, dt in rows if "nt_gemm256_kernel<false>" in n]
+        gf = gram_flops(w.n_steps * w.n_q, w.hidden) * w.n_layers
+        lines.append(f"Gram launches (all {w.n_layers} layers, all warmup tokens): {len(gram)}, "
+                     f"average {avg / 1e3:.1f} us for {gf / 1e9:.1f} GFLOP = "
+                     f"{gf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
+    proj = [dt for _, n, dt in rows
+            if "nt_gemm256_kernel<false, false>" in n or "g256_kernel<0>" in n]
     if proj:
         avg = sum(proj) / len(proj)
         pf = 2.0 * w.n_q * w.hidden * w.hidden
         lines.append(f"Output projections (post-absorption chunk): {len(proj)}, average "
                      f"{avg / 1e3:.1f} us for {pf / 1e9:.1f} GFLOP = "
                      f"{pf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
-    cw = [dt for _, n, dt in rows if "nt_gemm256_kernel<true>" in n]
+    cw = [dt for _, n, dt in rows if "g256_kernel<1>" in n]
     if cw:
         avg = sum(cw) / len(cw)
-        cf = 2.0 * 2.0 * w.n_layers * w.hidden ** 3  # two bf16 planes of C
-        lines.append(f"C W_o products (absorb, all layers, two bf16 planes of C): {len(cw)}, "
-                     f"average {avg / 1e3:.1f} us = {cf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
+        cf = 2.0 * 2.0 * w.n_layers * w.hidden ** 3  # two bf16 planes of the fp32 operand
+        lines.append(f"Y W_o and C W_o products (absorb, all layers, two bf16 planes of the fp32 "
+                     f"operand): {len(cw)}, average {avg / 1e3:.1f} us = "
+                     f"{cf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
     return "\n".join(lines) + "\n"
 
 
@@ -946,7 +955,7 @@ def main():
         "attn_kv_stream_gbs": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
         "attn_traffic_gbs": (round(attn_traffic / (attn_ms / n_launch * 1e-3) / 1e9, 1)
                              if attn_traffic else None),
-        "gram_traffic_bytes_per_launch": recorded_traffic("gram_kernel"),
+        "gram_traffic_bytes_per_launch": recorded_traffic("gram_t_kernel"),
         "post_absorb_chunk_ms": round(tot["post"] / K, 3),
         "selected_layers": [i for i, s in enumerate(sel) if s],
         "eps_rel_range": [min(eps), max(eps)],

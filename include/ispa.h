@@ -98,6 +98,31 @@ int ispa_attn_decomp(const void* q, int64_t n_q,
                      void* d_out, void* stream);
 
 /*
+ * The warmup step's attention with the statistics operands written
+ * feature-major (§3.1 items 1-2: both signals from the one pass, then the
+ * accumulated statistics over the tokens). Same inputs, arithmetic and
+ * errors as ispa_attn_decomp; outputs:
+ *   o_full, lse_full  as in ispa_attn_decomp (either may be NULL);
+ *   xt, dt            X = O_local and D = O_full - O_local, bf16, element
+ *                     (query q, feature f = head * head_dim + j) at
+ *                     [f * ld + q]: [n_heads * head_dim][ld], the same bf16
+ *                     values ispa_attn_decomp writes to o_local and d_out.
+ *                     Both required (ISPA_ERR_NULL). Columns >= n_q are not
+ *                     touched, so the warmup steps of a layer can be written
+ *                     side by side (xt + s * n_q with a common ld) and their
+ *                     statistics formed in one ispa_gram_accumulate_t call.
+ * ld >= n_q (ISPA_ERR_SHAPE), ld % 8 == 0 and xt, dt 16-byte aligned
+ * (ISPA_ERR_ALIGN).
+ */
+int ispa_attn_decomp_t(const void* q, int64_t n_q,
+                       const void* k_sink, const void* v_sink, int64_t n_sink,
+                       const void* k_cur, const void* v_cur, int64_t n_cur,
+                       const void* k_hist, const void* v_hist, int64_t n_hist,
+                       int n_heads, int head_dim, float sm_scale,
+                       void* o_full, float* lse_full, void* xt, void* dt, int64_t ld,
+                       void* stream);
+
+/*
  * Several attention calls in one launch (multi-instance batching: concurrent
  * streams, each with its own KV cache, as the paper's §3.3 instance-specific
  * state implies when several videos are generated at once). Each job is
@@ -204,6 +229,24 @@ int ispa_key_mean(const void* k_sink, int64_t n_sink, const void* k_cur, int64_t
 int ispa_gram_accumulate(const void* x, const void* d, int64_t n_tok, int h,
                          int n_batch, float* G, float* C, float* E,
                          int zero_first, void* stream);
+
+/*
+ * The warmup statistics from feature-major activations (the xt, dt of
+ * ispa_attn_decomp_t): for each of n_batch problems b,
+ *   G[b] (+)= X[b]^T X[b],  C[b] (+)= X[b]^T D[b],  E[b] (+)= D[b]^T D[b]
+ * with token t of feature f at xt[b][f * ld + t], t < n_tok
+ * (xt, dt: [n_batch][h][ld] bf16, batch stride h * ld). G, C, E as in
+ * ispa_gram_accumulate (E may be NULL; G and E exactly symmetric; fixed
+ * summation order). The contraction over tokens runs as a product of two
+ * token-contiguous operands on 256 x 256 output tiles.
+ * Errors: ISPA_ERR_NULL (xt, dt, G, C), ISPA_ERR_SHAPE (h < 1, n_tok < 0,
+ *   n_batch < 1, ld < n_tok), ISPA_ERR_UNSUPPORTED (h % 8 != 0, or one
+ *   layer's X^T of 2 GiB or more), ISPA_ERR_ALIGN (ld % 8 != 0 or a pointer
+ *   not 16-byte aligned).
+ */
+int ispa_gram_accumulate_t(const void* xt, const void* dt, int64_t n_tok, int64_t ld, int h,
+                           int n_batch, float* G, float* C, float* E, int zero_first,
+                           void* stream);
 
 /*
  * Closed-form absorb (§3.2, §4.1): for each layer l,

@@ -85,6 +85,11 @@ lib.ispa_session_layer_grouped.restype = _i
 lib.ispa_session_layer_grouped.argtypes = [_p, _i, _i, _p, _p, _p]
 lib.ispa_gram_accumulate.restype = _i
 lib.ispa_gram_accumulate.argtypes = [_p, _p, _i64, _i, _i, _p, _p, _p, _i, _p]
+lib.ispa_gram_accumulate_t.restype = _i
+lib.ispa_gram_accumulate_t.argtypes = [_p, _p, _i64, _i64, _i, _i, _p, _p, _p, _i, _p]
+lib.ispa_attn_decomp_t.restype = _i
+lib.ispa_attn_decomp_t.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _p, _i64, _i, _i, _f,
+                                   _p, _p, _p, _p, _i64, _p]
 lib.ispa_ridge_workspace_bytes.restype = _sz
 lib.ispa_ridge_workspace_bytes.argtypes = [_i, _i]
 lib.ispa_ridge_solve.restype = _i
@@ -197,7 +202,8 @@ EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram
             "ispa_quantize_fp8", "ispa_project_w8a8_workspace_bytes", "ispa_project_w8a8",
             "ispa_attn_fp8_workspace_bytes", "ispa_attn_decomp_fp8",
             "ispa_key_mean_workspace_bytes", "ispa_key_mean", "ispa_attn_decomp_grouped",
-            "ispa_project_grouped", "ispa_session_layer_grouped", "ispa_project_w8a8_noalloc")
+            "ispa_project_grouped", "ispa_session_layer_grouped", "ispa_project_w8a8_noalloc",
+            "ispa_attn_decomp_t", "ispa_gram_accumulate_t")
 
 
 class IspaError(RuntimeError):
@@ -274,6 +280,30 @@ def ispa_attn_decomp(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: 
     st = lib.ispa_attn_decomp(_ptr(q, torch.bfloat16, "q"), n_q, *segs, n_heads, head_dim,
                               float(sm_scale), *outs, _stream(stream))
     _check("ispa_attn_decomp", st)
+
+
+def ispa_attn_decomp_t(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: float, xt,
+                       dt, *, col: int = 0, o_full=None, lse_full=None, stream=None) -> None:
+    """The warmup step's attention with X = O_local and D written
+    feature-major: xt, dt are [H*d, ld] bf16 tensors and this call fills
+    their columns [col, col + n_q) (col % 8 == 0), so the warmup steps of one
+    layer can sit side by side; o_full / lse_full optional as in
+    ispa_attn_decomp."""
+    n_q, n_heads, head_dim, segs, outs = _attn_args(
+        q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist,
+        (None, None, None, None, o_full, lse_full, None))
+    h = n_heads * head_dim
+    for name, t in (("xt", xt), ("dt", dt)):
+        if t.dim() != 2 or t.shape[0] != h or t.shape[1] < col + n_q:
+            raise ValueError(f"{name}: expected [{h}, >= {col + n_q}]")
+    if dt.shape != xt.shape or col < 0:
+        raise ValueError("ispa_attn_decomp_t: xt / dt / col mismatch")
+    ld = xt.shape[1]
+    st = lib.ispa_attn_decomp_t(_ptr(q, torch.bfloat16, "q"), n_q, *segs, n_heads, head_dim,
+                                float(sm_scale), outs[4], outs[5],
+                                _ptr(xt, torch.bfloat16, "xt") + 2 * col,
+                                _ptr(dt, torch.bfloat16, "dt") + 2 * col, ld, _stream(stream))
+    _check("ispa_attn_decomp_t", st)
 
 
 def ispa_attn_decomp_grouped(calls, sm_scale: float, *, stream=None) -> None:
@@ -386,6 +416,25 @@ def ispa_gram_accumulate(x, d, G, C, E=None, *, zero_first: bool = False, stream
                                   _ptr(C, torch.float32, "C"), _ptr(E, torch.float32, "E"),
                                   1 if zero_first else 0, _stream(stream))
     _check("ispa_gram_accumulate", st)
+
+
+def ispa_gram_accumulate_t(xt, dt, n_tok: int, G, C, E=None, *, zero_first: bool = False,
+                           stream=None) -> None:
+    """xt, dt [B, h, ld] (or [h, ld]) bf16 feature-major activations, the
+    first n_tok columns used; G, C, E [B, h, h] fp32."""
+    if xt.dim() == 2:
+        xt, dt = xt.unsqueeze(0), dt.unsqueeze(0)
+        G, C = G.unsqueeze(0), C.unsqueeze(0)
+        E = None if E is None else E.unsqueeze(0)
+    b, h, ld = xt.shape
+    if dt.shape != xt.shape or G.shape != (b, h, h) or C.shape != (b, h, h) or (
+            E is not None and E.shape != (b, h, h)):
+        raise ValueError("ispa_gram_accumulate_t: shape mismatch")
+    st = lib.ispa_gram_accumulate_t(_ptr(xt, torch.bfloat16, "xt"), _ptr(dt, torch.bfloat16, "dt"),
+                                    n_tok, ld, h, b, _ptr(G, torch.float32, "G"),
+                                    _ptr(C, torch.float32, "C"), _ptr(E, torch.float32, "E"),
+                                    1 if zero_first else 0, _stream(stream))
+    _check("ispa_gram_accumulate_t", st)
 
 
 def ispa_ridge_workspace_bytes(n_layers: int, h: int) -> int:

@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libispa.so")
 
 SOURCES = ["attn_decomp.hip", "gram.hip", "gemm_f32.hip", "solve.hip", "ispa_api.hip",
            "kv_cache.hip", "session.hip", "nt_gemm.hip", "w8a8.hip",
-           "attn_fp8.hip", "noalloc.hip"]
+           "attn_fp8.hip", "noalloc.hip", "gemm256.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -201,6 +201,37 @@ __device__ __forceinline__ void load_o(const uint16_t* in, f32x16* o, int64_t qi
   }
 }
 
+// Feature-major forms of store_o / load_o: element (query qi, feature
+// head * D + d) at out[(head * D + d) * ld + qi]. Consecutive lanes hold
+// consecutive queries, so each store covers 64 contiguous bytes of two rows.
+template <int D>
+__device__ __forceinline__ void store_ot(uint16_t* out, const f32x16* o, int64_t qi, int64_t ld,
+                                         int head, int hf) {
+  uint16_t* col = out + static_cast<int64_t>(head) * D * ld + qi;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        col[static_cast<int64_t>(32 * db + 8 * g + 4 * hf + r) * ld] =
+            f32_to_bf16_bits(o[db][4 * g + r]);
+}
+
+template <int D>
+__device__ __forceinline__ void load_ot(const uint16_t* in, f32x16* o, int64_t qi, int64_t ld,
+                                        int head, int hf) {
+  const uint16_t* col = in + static_cast<int64_t>(head) * D * ld + qi;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        o[db][4 * g + r] =
+            bf16_bits_to_f32(col[static_cast<int64_t>(32 * db + 8 * g + 4 * hf + r) * ld]);
+}
+
 // One workgroup's work item `work` (head x query tile) of one attention call.
 template <int D, bool F8>
 __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) {
@@ -596,9 +627,11 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
   // while the history phase runs, so D is formed against exactly that X: it
   // is parked in an output row this lane owns (O_local if requested, else
   // O_full, else D; each is written with its final value only after the
-  // parked X has been read back). With none of them requested, no merge is
-  // formed and X is not needed.
+  // parked X has been read back), or, with none of those requested, in its
+  // feature-major copy. With none of them requested, no merge is formed and
+  // X is not needed.
   uint16_t* const park = p.o_local ? p.o_local : (p.o_full ? p.o_full : p.d_out);
+  const bool park_t = park == nullptr && p.xt != nullptr;
   TrOff voff[NB];  // lane offsets of the V^T operand reads, per 32-wide d block
 #pragma unroll
   for (int b = 0; b < NB; ++b) voff[b] = tr_offsets<D>(32 * b, lane);
@@ -668,7 +701,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
           const float inv = s_inv_loc[prow + 32 * qb + l32];
 #pragma unroll
           for (int b = 0; b < NB; ++b) oacc[qb][b] *= inv;
-          if (qvalid[qb] && park) store_o<D>(park, oacc[qb], qi[qb], rs, head, hf);
+          if (qvalid[qb]) {
+            if (park) store_o<D>(park, oacc[qb], qi[qb], rs, head, hf);
+            if (p.xt) store_ot<D>(p.xt, oacc[qb], qi[qb], p.ldt, head, hf);
+          }
 #pragma unroll
           for (int b = 0; b < NB; ++b) oacc[qb][b] = f32x16{};
         }
@@ -698,13 +734,17 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
 #pragma unroll
     for (int b = 0; b < NB; ++b) oacc[qb][b] *= inv;
     if (p.o_hist) store_o<D>(p.o_hist, oacc[qb], qi[qb], rs, head, hf);
-    if (!park) continue;
+    if (!park && !park_t) continue;
     const float w_h = s_wh[prow + 32 * qb + l32];
     f32x16 xl[NB];
-    load_o<D>(park, xl, qi[qb], rs, head, hf);
+    if (park)
+      load_o<D>(park, xl, qi[qb], rs, head, hf);
+    else
+      load_ot<D>(p.xt, xl, qi[qb], p.ldt, head, hf);
 #pragma unroll
     for (int b = 0; b < NB; ++b) oacc[qb][b] = (oacc[qb][b] - xl[b]) * w_h;
     if (p.d_out) store_o<D>(p.d_out, oacc[qb], qi[qb], rs, head, hf);
+    if (p.dt) store_ot<D>(p.dt, oacc[qb], qi[qb], p.ldt, head, hf);
     if (p.o_full) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) oacc[qb][b] += xl[b];

@@ -422,9 +422,29 @@ hipError_t launch_gram(const GramParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Fraction of the compute units busy, averaged over the rounds, when `tiles`
+// equal workgroups (one per CU) run on `cus` compute units.
+static double round_fill(int64_t tiles, int cus) {
+  const int64_t rounds = (tiles + cus - 1) / cus;
+  return rounds ? static_cast<double>(tiles) / static_cast<double>(rounds * cus) : 0.0;
+}
+
 hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, int h_in,
                           int h_out, hipStream_t stream) {
-  if (nt_gemm256_supported(h_in)) return launch_nt_gemm256_bf16(x, w, y, n, h_in, h_out, stream);
+  if (nt_gemm256_supported(h_in)) {
+    // 256 x 256 tiles run each FLOP ~1.4x faster than 256 x 128 ones (fewer
+    // operand bytes and barriers per MFMA) but come in half the number:
+    // take them when that still wins after the partial last round
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    const int64_t rows = (n + 255) / 256;
+    const double big = 1.4 * round_fill(rows * ((h_out + 255) / 256), cus);
+    const double small = round_fill(rows * ((h_out + 127) / 128), cus);
+    if (big > small) return launch_g256_bf16(x, w, y, n, h_in, h_out, stream);
+    return launch_nt_gemm256_bf16(x, w, y, n, h_in, h_out, stream);
+  }
   const int64_t tiles = ((n + kT - 1) / kT) * ((h_out + kT - 1) / kT);
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL(nt_gemm_kernel<false>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0,
@@ -439,7 +459,7 @@ hipError_t launch_split_nt_gemm_f32(const float* c, uint16_t* hi, uint16_t* lo,
   const int64_t count = hh * batch;
   if (count == 0) return hipSuccess;
   hipLaunchKernelGGL(split_bf16_kernel, dim3(4096), dim3(256), 0, stream, c, hi, lo, count);
-  if (nt_gemm256_supported(h)) return launch_nt_gemm256_split_f32(hi, lo, w, y, h, batch, stream);
+  if (nt_gemm256_supported(h)) return launch_g256_split_f32(hi, lo, w, y, h, batch, stream);
   const int64_t tiles = static_cast<int64_t>((h + kT - 1) / kT) * ((h + kT - 1) / kT);
   hipLaunchKernelGGL(nt_gemm_kernel<true>, dim3(static_cast<unsigned>(tiles), batch),
                      dim3(kThreads), 0, stream, hi, lo, hh, w, hh, static_cast<void*>(y), hh,

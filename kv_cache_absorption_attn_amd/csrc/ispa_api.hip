@@ -195,7 +195,8 @@ int attn_setup(const void* q, int64_t n_q, const void* k_sink, const void* v_sin
                const void* k_hist, const void* v_hist, int64_t n_hist, int n_heads,
                int head_dim, float sm_scale, void* o_local, float* lse_local, void* o_hist,
                float* lse_hist, void* o_full, float* lse_full, void* d_out,
-               ispa::AttnParams* out, bool* run) {
+               ispa::AttnParams* out, bool* run, void* xt = nullptr, void* dt = nullptr,
+               int64_t ldt = 0) {
   *run = false;
   if (n_q < 0 || n_sink < 0 || n_cur < 0 || n_hist < 0 || n_heads < 1) return ISPA_ERR_SHAPE;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return ISPA_ERR_SHAPE;
@@ -204,11 +205,12 @@ int attn_setup(const void* q, int64_t n_q, const void* k_sink, const void* v_sin
   if ((n_sink > 0 && (!k_sink || !v_sink)) || (n_cur > 0 && (!k_cur || !v_cur)) ||
       (n_hist > 0 && (!k_hist || !v_hist)))
     return ISPA_ERR_NULL;
-  if (!o_local && !lse_local && !o_hist && !lse_hist && !o_full && !lse_full && !d_out)
+  if (!o_local && !lse_local && !o_hist && !lse_hist && !o_full && !lse_full && !d_out && !xt &&
+      !dt)
     return ISPA_ERR_NULL;
   if (n_sink + n_cur < 1) return ISPA_ERR_SHAPE;
   const void* ptrs[] = {q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, o_local, lse_local,
-                        o_hist, lse_hist, o_full, lse_full, d_out};
+                        o_hist, lse_hist, o_full, lse_full, d_out, xt, dt};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return ISPA_ERR_ALIGN;
   const int64_t qtiles = (n_q + ispa::attn_q_tile_min() - 1) / ispa::attn_q_tile_min();
@@ -236,9 +238,12 @@ int attn_setup(const void* q, int64_t n_q, const void* k_sink, const void* v_sin
   p.o_full = static_cast<uint16_t*>(o_full);
   p.lse_full = lse_full;
   p.d_out = static_cast<uint16_t*>(d_out);
-  const bool only_full = !o_local && !lse_local && !o_hist && !lse_hist && !d_out;
+  p.xt = static_cast<uint16_t*>(xt);
+  p.dt = static_cast<uint16_t*>(dt);
+  p.ldt = ldt;
+  const bool only_full = !o_local && !lse_local && !o_hist && !lse_hist && !d_out && !xt && !dt;
   p.mode = only_full ? 1 : 0;
-  p.need_hist = (o_hist || lse_hist || o_full || lse_full || d_out) ? 1 : 0;
+  p.need_hist = (o_hist || lse_hist || o_full || lse_full || d_out || dt) ? 1 : 0;
   *out = p;
   *run = true;
   return ISPA_OK;
@@ -287,6 +292,23 @@ int ispa_attn_decomp(const void* q, int64_t n_q, const void* k_sink, const void*
   const int st = attn_setup(q, n_q, k_sink, v_sink, n_sink, k_cur, v_cur, n_cur, k_hist, v_hist,
                             n_hist, n_heads, head_dim, sm_scale, o_local, lse_local, o_hist,
                             lse_hist, o_full, lse_full, d_out, &p, &run);
+  if (st != ISPA_OK || !run) return st;
+  return hip_status(ispa::launch_attn_decomp(p, head_dim, as_stream(stream)));
+}
+
+int ispa_attn_decomp_t(const void* q, int64_t n_q, const void* k_sink, const void* v_sink,
+                       int64_t n_sink, const void* k_cur, const void* v_cur, int64_t n_cur,
+                       const void* k_hist, const void* v_hist, int64_t n_hist, int n_heads,
+                       int head_dim, float sm_scale, void* o_full, float* lse_full, void* xt,
+                       void* dt, int64_t ld, void* stream) {
+  if (!xt || !dt) return ISPA_ERR_NULL;
+  if (ld < n_q || ld < 1) return ISPA_ERR_SHAPE;
+  if (ld % 8 != 0) return ISPA_ERR_ALIGN;
+  ispa::AttnParams p{};
+  bool run = false;
+  const int st = attn_setup(q, n_q, k_sink, v_sink, n_sink, k_cur, v_cur, n_cur, k_hist, v_hist,
+                            n_hist, n_heads, head_dim, sm_scale, nullptr, nullptr, nullptr,
+                            nullptr, o_full, lse_full, nullptr, &p, &run, xt, dt, ld);
   if (st != ISPA_OK || !run) return st;
   return hip_status(ispa::launch_attn_decomp(p, head_dim, as_stream(stream)));
 }
@@ -431,6 +453,24 @@ int ispa_gram_accumulate(const void* x, const void* d, int64_t n_tok, int h, int
   p.zero_first = zero_first ? 1 : 0;
   if (n_tok == 0 && !zero_first) return ISPA_OK;
   return hip_status(ispa::launch_gram(p, as_stream(stream)));
+}
+
+int ispa_gram_accumulate_t(const void* xt, const void* dt, int64_t n_tok, int64_t ld, int h,
+                           int n_batch, float* G, float* C, float* E, int zero_first,
+                           void* stream) {
+  if (!xt || !dt || !G || !C) return ISPA_ERR_NULL;
+  if (h < 1 || n_tok < 0 || n_batch < 1 || ld < n_tok || ld < 1) return ISPA_ERR_SHAPE;
+  if (h % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (ld % 8 != 0 || !aligned16(xt) || !aligned16(dt) || !aligned16(G) || !aligned16(C) ||
+      (E && !aligned16(E)))
+    return ISPA_ERR_ALIGN;
+  // buffer offsets of the loads are 32-bit: one layer's X^T must stay below 2 GiB
+  if (static_cast<int64_t>(h) * ld * 2 > INT32_MAX || n_tok > INT32_MAX)
+    return ISPA_ERR_UNSUPPORTED;
+  if (n_tok == 0 && !zero_first) return ISPA_OK;
+  return hip_status(ispa::launch_gram_t(static_cast<const uint16_t*>(xt),
+                                        static_cast<const uint16_t*>(dt), n_tok, ld, h, n_batch, G,
+                                        C, E, zero_first, as_stream(stream)));
 }
 
 size_t ispa_ridge_workspace_bytes(int n_layers, int h) {

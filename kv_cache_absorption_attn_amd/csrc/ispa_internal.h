@@ -22,6 +22,12 @@ struct AttnParams {
   uint16_t* o_full;
   float* lse_full;
   uint16_t* d_out;
+  // feature-major copies of X = O_local and of D (element (query q, feature
+  // f) at [f * ldt + q]), the operands of the feature-major Gram; either may
+  // be null
+  uint16_t* xt;
+  uint16_t* dt;
+  int64_t ldt;
   int n_qtiles;
   int mode;                  // 0: local / history split + merge; 1: one pass (full only)
   int need_hist;             // split mode: history phase and merge needed
@@ -193,5 +199,22 @@ hipError_t launch_nt_gemm256_split_f32(const uint16_t* hi, const uint16_t* lo, c
                                        float* y, int h, int batch, hipStream_t stream);
 hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
                           int h_in, int h_out, hipStream_t stream);
+
+// The 256 x 256-tile NT GEMM (gemm256.hip).
+// Y = X W^T, bf16 out; contraction length a multiple of 8 (any length works;
+// the last stage is masked).
+hipError_t launch_g256_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
+                            int h_in, int h_out, hipStream_t stream);
+// Y[b] = (hi[b] + lo[b]) W[b]^T in fp32 for h x h operands (an fp32 matrix
+// held as two bf16 planes times a bf16 matrix).
+hipError_t launch_g256_split_f32(const uint16_t* hi, const uint16_t* lo, const uint16_t* w,
+                                 float* y, int h, int batch, hipStream_t stream);
+// Warmup statistics from feature-major activations: X^T, D^T [batch][h][ld]
+// bf16 (token t of feature f at f * ld + t, n_tok <= ld, ld % 8 == 0):
+// G = X^T X, C = X^T D, E = D^T D (fp32 [batch][h][h]; E may be null),
+// accumulated or overwritten (zero_first); G and E exactly symmetric.
+hipError_t launch_gram_t(const uint16_t* xt, const uint16_t* dt, int64_t n_tok, int64_t ld, int h,
+                         int batch, float* G, float* C, float* E, int zero_first,
+                         hipStream_t stream);
 
 }  // namespace ispa

@@ -71,6 +71,31 @@ def test_attn_validation():
     assert attn(ol=MIS) == ALIGN
 
 
+def test_feature_major_validation():
+    """The feature-major attention and Gram entry points: argument checks
+    that return before any launch."""
+    L = _lib.lib
+    seg = (A, 16, A, A, 8, A, A, 8, 0, 0, 0, 2, 128, 0.1)
+
+    def at(of=A, lf=0, xt=A, dt=A, ld=16):
+        return L.ispa_attn_decomp_t(*seg, of, lf, xt, dt, ld, 0)
+    assert at(xt=0) == NULL and at(dt=0) == NULL
+    assert at(ld=8) == SHAPE              # ld < n_q
+    assert at(ld=20) == ALIGN             # ld % 8
+    assert at(xt=MIS) == ALIGN
+    assert L.ispa_attn_decomp_t(A, 16, A, A, 8, A, A, 8, 0, 0, 0, 2, 96, 0.1, A, 0, A, A, 16,
+                                0) == UNSUP
+    gt = L.ispa_gram_accumulate_t
+    assert gt(0, A, 100, 104, 128, 1, A, A, 0, 1, 0) == NULL
+    assert gt(A, A, 100, 96, 128, 1, A, A, 0, 1, 0) == SHAPE      # ld < n_tok
+    assert gt(A, A, 100, 104, 120, 0, A, A, 0, 1, 0) == SHAPE     # no batch
+    assert gt(A, A, 100, 104, 124, 1, A, A, 0, 1, 0) == UNSUP     # h % 8
+    assert gt(A, A, 100, 102, 128, 1, A, A, 0, 1, 0) == ALIGN     # ld % 8
+    assert gt(A, A, 100, 104, 128, 1, MIS, A, 0, 1, 0) == ALIGN
+    assert gt(A, A, 100, 2 ** 20, 1024, 1, A, A, 0, 1, 0) == UNSUP  # 2 GiB per layer
+    assert gt(A, A, 0, 104, 128, 1, A, A, 0, 0, 0) == OK          # nothing to add
+
+
 def test_gram_validation():
     g = _lib.lib.ispa_gram_accumulate
     assert g(0, A, 10, 128, 1, A, A, 0, 0, 0) == NULL

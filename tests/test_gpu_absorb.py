@@ -265,7 +265,8 @@ def _synthetic_stats(L, h, n, seed):
     return G, C, E, dev_bf16(np.stack(Ws)), hostside
 
 
-@pytest.mark.parametrize("L,h,n", [(1, 128, 300), (3, 320, 500), (2, 64, 50), (2, 256, 400)])
+@pytest.mark.parametrize("L,h,n", [(1, 128, 300), (3, 320, 500), (2, 64, 50), (2, 256, 400),
+                                   (2, 200, 300)])
 def test_ridge_and_score(L, h, n):
     log(f"ridge L={L} h={h} n={n}")
     lam = 1e-2
@@ -392,7 +393,8 @@ def test_apply_bit_exact():
         np.testing.assert_array_equal(got[l], exp)
 
 
-@pytest.mark.parametrize("n,h_in,h_out", [(200, 128, 192), (4680, 1536, 1536), (7, 64, 64)])
+@pytest.mark.parametrize("n,h_in,h_out", [(200, 128, 192), (4680, 1536, 1536), (7, 64, 64),
+                                         (4680, 5120, 5120), (1000, 200, 72)])
 def test_project(n, h_in, h_out):
     log(f"project {n}x{h_in}->{h_out}")
     x = wl.random_bf16((n, h_in), 0.5, 51)
