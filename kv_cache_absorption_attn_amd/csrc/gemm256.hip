@@ -13,16 +13,19 @@
 // 128 FLOP/B) halves the L2 -> CU stream of a 256 x 128 tile at the same
 // rate.
 //
-// k-stages of 32 (64-byte LDS rows) go through a 4-slot LDS ring filled three
-// stages ahead by direct-to-LDS buffer loads (lds_dma_asm.h): each wave waits
-// for its own loads of the stage it is about to read (vmcnt), one plain
-// barrier per stage publishes them and frees the slot that the next issue
-// overwrites. A row's 16-byte chunk c is stored at chunk position
-// c ^ ((row >> 2) & 3), so the 16 rows of one quarter-wave's fragment reads
-// cover all 64 banks once. Rows past the matrix re-load its last row (their
-// results are never stored). A contraction length that is not a multiple of
-// 32 ends in a stage whose chunks past the end re-load the last valid chunk
-// and whose fragment elements past the end are zeroed in registers.
+// k-stages of 64 (128-byte LDS rows: each row of a stage is one whole L2
+// line, so a stage takes half the cache requests of two 64-byte stages) go
+// through two 64 KB LDS slots filled by direct-to-LDS buffer loads
+// (lds_dma_asm.h) one stage ahead: each wave waits for its own loads of the
+// stage it is about to read (vmcnt), one plain barrier per stage publishes
+// them and frees the other slot, whose refill is spread between the first
+// MFMAs. A row's 16-byte chunk c is stored at chunk position c ^ ((row >> 1)
+// & 7), so the 16 rows of one quarter-wave's fragment reads cover all 64
+// banks once. Rows past the matrix re-load its last row (their results are
+// never stored). A contraction length that is not a multiple of 64 ends in a
+// stage whose chunks past the end re-load the last valid chunk and whose
+// fragment elements past the end are zeroed in registers. (The tile function
+// also takes 32-k stages in a 4-slot ring filled three stages ahead.)
 
 #include "device_common.h"
 #include "ispa_internal.h"
@@ -31,16 +34,13 @@
 namespace ispa {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kBM = 256, kBN = 256;
+// k per ring stage: 64 (128-byte rows, whole L2 lines, two 64 KB slots)
+// measured 1.03-1.3x the rate of 32 (64-byte rows, four 32 KB slots) on the
+// projection, the Gram and the split products
+constexpr int kStageK = 64;
 constexpr int kThreads = 512;
-constexpr int kRowE = kBK;   // bf16 per LDS row (64 bytes)
 constexpr int kGroupM = 4;   // row tiles per L2 group
-
-__device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ ((row >> 2) & 3); }
-
-__device__ __forceinline__ bf16x8 frag(const uint16_t* slot, int row, int pos) {
-  return *reinterpret_cast<const bf16x8*>(slot + row * kRowE + 8 * pos);
-}
 
 // Zero the elements of a fragment (8 consecutive k from k0) at k >= k_end.
 __device__ __forceinline__ bf16x8 mask_k(bf16x8 f, int k0, int k_end) {
@@ -78,11 +78,22 @@ namespace {
 
 enum { kOutBf16 = 0, kOutF32 = 1, kAccF32 = 2 };
 
-template <int OUT>
+template <int OUT, int KB>
 __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const int tn) {
-  constexpr int NS = 4;  // ring slots
-  __shared__ __attribute__((aligned(16))) uint16_t sa[NS][kBM * kRowE];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[NS][kBN * kRowE];
+  static_assert(KB == 32 || KB == 64, "stages of 32 or 64 k");
+  constexpr int NS = KB == 32 ? 4 : 2;   // ring slots (128 KB of LDS either way)
+  constexpr int CPR = KB / 8;            // 16-byte chunks of an LDS row
+  constexpr int RPI = 64 / CPR;          // rows one load instruction fills
+  constexpr int LPW = 32 / RPI;          // load instructions a wave issues per operand
+  constexpr int LS = 2 * LPW;            // ... per stage
+  constexpr int KS = KB / 16;            // MFMA k-steps of a stage
+  __shared__ __attribute__((aligned(16))) uint16_t sa[NS][kBM * KB];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[NS][kBN * KB];
+  // chunk c of row r sits at position c ^ swz(r): the 16 rows of a
+  // quarter-wave's fragment reads then cover the 64 banks once
+  auto pos_of = [](int r, int c) {
+    return KB == 32 ? c ^ ((r >> 2) & 3) : c ^ ((r >> 1) & 7);
+  };
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, l32 = lane % 32, hf = lane / 32;
@@ -90,56 +101,51 @@ __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const
   const int64_t m0 = static_cast<int64_t>(tm) * kBM;
   const int n0 = tn * kBN;
 
-  const int nk = (p.k + kBK - 1) / kBK;
-  const bool tail = (p.k % kBK) != 0;
+  const int nk = (p.k + KB - 1) / KB;
+  const bool tail = (p.k % KB) != 0;
   const int nst = p.a2 ? 2 * nk : nk;
   const u32x4 ra1 = desc_of(p.a);
   const u32x4 ra2 = desc_of(p.a2 ? p.a2 : p.a);
   const u32x4 rb = desc_of(p.b);
 
   // wave w loads A rows [32 w, 32 w + 32) and B rows [32 w, 32 w + 32) of a
-  // stage: two instructions each (16 rows x 64 bytes); lane -> (row lane / 4,
-  // chunk position lane % 4)
-  uint32_t va[2], vb[2];
-  int arow[2], brow[2];
-  const int p4 = lane % 4;
+  // stage, LPW instructions each; lane -> (row lane / CPR, position lane % CPR)
+  uint32_t va[LPW], vb[LPW];
+  int lrow[LPW];
+  const int pc = lane % CPR;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = wave * 32 + 16 * j + lane / 4;
+  for (int j = 0; j < LPW; ++j) {
+    const int row = wave * 32 + RPI * j + lane / CPR;
+    lrow[j] = row;
     int64_t gr = m0 + row;
     if (gr > p.m - 1) gr = p.m - 1;
-    arow[j] = row;
-    va[j] = static_cast<uint32_t>(gr * p.lda * 2 + 16 * chunk_pos(row, p4));
+    va[j] = static_cast<uint32_t>(gr * p.lda * 2 + 16 * pos_of(row, pc));
     int gb = n0 + row;
     if (gb > p.n - 1) gb = p.n - 1;
-    brow[j] = row;
-    vb[j] = static_cast<uint32_t>(static_cast<int64_t>(gb) * p.ldb * 2 + 16 * chunk_pos(row, p4));
+    vb[j] = static_cast<uint32_t>(static_cast<int64_t>(gb) * p.ldb * 2 + 16 * pos_of(row, pc));
   }
   // the last stage of a ragged contraction: chunks that start past the end
   // re-load the last valid chunk (in bounds; masked after the read)
   const int k_last_chunk = ((p.k - 1) / 8) * 8;
   auto tail_off = [&](uint32_t v, int row, int kst) {
-    const int c = chunk_pos(row, p4);
-    int k0 = kst * kBK + 8 * c;
+    const int c = pos_of(row, pc);
+    int k0 = kst * KB + 8 * c;
     if (k0 > k_last_chunk) k0 = k_last_chunk;
     return v - 16 * c + 2 * k0;   // same row, chunk at k0 (stage offset not added)
   };
-  auto issue = [&](int s, uint16_t* da, uint16_t* db) {
+  // load j (0 .. LS - 1) of stage s into slot (da, db): j < LPW A, else B
+  auto dma = [&](int s, uint16_t* da, uint16_t* db, int j) __attribute__((always_inline)) {
     const int kst = s >= nk ? s - nk : s;
-    const u32x4 r = s >= nk ? ra2 : ra1;
-    if (tail && kst == nk - 1) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        dma16_asm(r, da + (wave * 32 + 16 * j) * kRowE, tail_off(va[j], arow[j], kst), 0);
-        dma16_asm(rb, db + (wave * 32 + 16 * j) * kRowE, tail_off(vb[j], brow[j], kst), 0);
-      }
+    const bool t = tail && kst == nk - 1;
+    const int jj = j % LPW;
+    const int row0 = wave * 32 + RPI * jj;
+    if (j < LPW) {
+      const u32x4 r = s >= nk ? ra2 : ra1;
+      dma16_asm(r, da + row0 * KB, t ? tail_off(va[jj], lrow[jj], kst) : va[jj],
+                t ? 0 : kst * 2 * KB);
     } else {
-      const int soff = kst * 64;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        dma16_asm(r, da + (wave * 32 + 16 * j) * kRowE, va[j], soff);
-        dma16_asm(rb, db + (wave * 32 + 16 * j) * kRowE, vb[j], soff);
-      }
+      dma16_asm(rb, db + row0 * KB, t ? tail_off(vb[jj], lrow[jj], kst) : vb[jj],
+                t ? 0 : kst * 2 * KB);
     }
   };
 
@@ -149,79 +155,80 @@ __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  int ar[4], br[2], apos[4][2], bpos[2][2];
+  int ar[4], br[2], apos[4][KS], bpos[2][KS];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     ar[i] = wm * 128 + i * 32 + l32;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) apos[i][kk] = chunk_pos(ar[i], 2 * kk + hf);
+    for (int kk = 0; kk < KS; ++kk) apos[i][kk] = pos_of(ar[i], 2 * kk + hf);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     br[j] = wn * 64 + j * 32 + l32;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) bpos[j][kk] = chunk_pos(br[j], 2 * kk + hf);
+    for (int kk = 0; kk < KS; ++kk) bpos[j][kk] = pos_of(br[j], 2 * kk + hf);
   }
+  auto frag_at = [](const uint16_t* slot, int row, int pos) {
+    return *reinterpret_cast<const bf16x8*>(slot + row * KB + 8 * pos);
+  };
 
-  for (int s = 0; s < NS - 1 && s < nst; ++s) issue(s, sa[s], sb[s]);
+  for (int s = 0; s < NS - 1 && s < nst; ++s)
+#pragma unroll
+    for (int j = 0; j < LS; ++j) dma(s, sa[s], sb[s], j);
 
   auto stage = [&](int s, const uint16_t* __restrict__ ca, const uint16_t* __restrict__ cb,
                    uint16_t* __restrict__ na, uint16_t* __restrict__ nb)
       __attribute__((always_inline)) {
-    // stages s + 1 and s + 2 may still be in flight (4 loads each)
-    if (s + 2 < nst)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (s + 1 < nst)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
+    // this wave's loads of stage s have landed; the stages issued after it
+    // (up to NS - 2 of them, LS loads each) may stay in flight
+    if constexpr (NS == 4) {
+      if (s + 2 < nst)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (s + 1 < nst)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     // a plain barrier: __syncthreads() would add a wait for every load in
-    // flight, including the two stages issued ahead
+    // flight, including the stages issued ahead
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    bf16x8 av[2][4], bv[2][2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[kk][i] = frag(ca, ar[i], apos[i][kk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bv[kk][j] = frag(cb, br[j], bpos[j][kk]);
-    }
     const int kst = s >= nk ? s - nk : s;
-    if (tail && kst == nk - 1) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int k0 = kst * kBK + 16 * kk + 8 * hf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[kk][i] = mask_k(av[kk][i], k0, p.k);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bv[kk][j] = mask_k(bv[kk][j], k0, p.k);
-      }
-    }
+    const bool mask = tail && kst == nk - 1;
     const bool refill = s + NS - 1 < nst;
-    // the refill of the slot freed by the previous stage, spread between the
-    // first MFMAs
+    // two k-steps at a time: their fragments, then their MFMAs, the refill of
+    // the slot freed by the previous stage spread between the first ones
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int h2 = 0; h2 < KS / 2; ++h2) {
+      bf16x8 av[2][4], bv[2][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int q = 0; q < 2; ++q) {
+        const int kk = 2 * h2 + q;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = mfma32x32x16(av[kk][i], bv[kk][j], acc[i][j]);
-          if (kk == 0 && j == 1 && refill) {
-            const int s3 = s + NS - 1;
-            const int k3 = s3 >= nk ? s3 - nk : s3;
-            const u32x4 r3 = s3 >= nk ? ra2 : ra1;
-            const bool t3 = tail && k3 == nk - 1;
-            const int jj = i / 2;
-            if (i % 2 == 0)
-              dma16_asm(r3, na + (wave * 32 + 16 * jj) * kRowE,
-                        t3 ? tail_off(va[jj], arow[jj], k3) : va[jj], t3 ? 0 : k3 * 64);
-            else
-              dma16_asm(rb, nb + (wave * 32 + 16 * jj) * kRowE,
-                        t3 ? tail_off(vb[jj], brow[jj], k3) : vb[jj], t3 ? 0 : k3 * 64);
-          }
+        for (int i = 0; i < 4; ++i) av[q][i] = frag_at(ca, ar[i], apos[i][kk]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bv[q][j] = frag_at(cb, br[j], bpos[j][kk]);
+        if (mask) {
+          const int k0 = kst * KB + 16 * kk + 8 * hf;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) av[q][i] = mask_k(av[q][i], k0, p.k);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) bv[q][j] = mask_k(bv[q][j], k0, p.k);
         }
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc[i][j] = mfma32x32x16(av[q][i], bv[q][j], acc[i][j]);
+            const int u = (h2 * 2 + q) * 8 + i * 2 + j;
+            if (u < LS && refill) dma(s + NS - 1, na, nb, u);
+          }
+    }
   };
   for (int s0 = 0; s0 < nst; s0 += NS) {
 #pragma unroll
@@ -299,7 +306,7 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, in
   *tn = (t % per_group) / gm;
 }
 
-template <int OUT>
+template <int OUT, int KB>
 __global__ __launch_bounds__(kThreads, 1) void g256_kernel(const G256Args p, int64_t a_bs,
                                                            int64_t a2_bs, int64_t b_bs,
                                                            int64_t y_bs) {
@@ -313,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void g256_kernel(const G256Args p, int
   q.a2 = p.a2 ? p.a2 + b * a2_bs : nullptr;
   q.b = p.b + b * b_bs;
   q.y = static_cast<char*>(p.y) + b * y_bs * (OUT == kOutBf16 ? 2 : 4);
-  g256_tile<OUT>(q, tm, tn);
+  g256_tile<OUT, KB>(q, tm, tn);
 }
 
 // The warmup statistics of one batch entry (layer) per blockIdx.y from
@@ -332,6 +339,7 @@ struct GramTArgs {
   int zero_first;
 };
 
+template <int KB>
 __global__ __launch_bounds__(kThreads, 1) void gram_t_kernel(const GramTArgs p, int nt,
                                                              int n_tiles) {
   const int t = xcd_remap(blockIdx.x, n_tiles);
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void gram_t_kernel(const GramTArgs p, 
   q.ldy = p.h;
   q.sym = job != 1;
   q.zero_first = p.zero_first;
-  g256_tile<kAccF32>(q, tm, tn);
+  g256_tile<kAccF32, KB>(q, tm, tn);
 }
 
 // Buffer-load offsets are 32 bit: rows of A run in blocks whose bytes stay
@@ -389,7 +397,7 @@ hipError_t launch_g256(G256Args a, int batch, int64_t a_bs, int64_t b_bs, int64_
     if (a.a2) blk.a2 = a.a2 + r0 * a.lda;
     blk.y = static_cast<char*>(a.y) + r0 * a.ldy * ys;
     const int64_t tiles = ((blk.m + kBM - 1) / kBM) * ((a.n + kBN - 1) / kBN);
-    hipLaunchKernelGGL((g256_kernel<OUT>), dim3(static_cast<unsigned>(tiles), batch),
+    hipLaunchKernelGGL((g256_kernel<OUT, kStageK>), dim3(static_cast<unsigned>(tiles), batch),
                        dim3(kThreads), 0, stream, blk, a_bs, a_bs, b_bs, y_bs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -439,8 +447,8 @@ hipError_t launch_gram_t(const uint16_t* xt, const uint16_t* dt, int64_t n_tok, 
   const int n_sym = nt * (nt + 1) / 2;
   const int n_tiles = nt * nt + n_sym + (E ? n_sym : 0);
   GramTArgs p{xt, dt, ld, static_cast<int64_t>(h) * ld, n_tok, h, G, C, E, zero_first};
-  hipLaunchKernelGGL(gram_t_kernel, dim3(n_tiles, batch), dim3(kThreads), 0, stream, p, nt,
-                     n_tiles);
+  hipLaunchKernelGGL(gram_t_kernel<kStageK>, dim3(n_tiles, batch), dim3(kThreads), 0, stream, p,
+                     nt, n_tiles);
   return hipGetLastError();
 }
 
