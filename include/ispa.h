@@ -102,7 +102,8 @@ int ispa_attn_decomp(const void* q, int64_t n_q,
  * feature-major (§3.1 items 1-2: both signals from the one pass, then the
  * accumulated statistics over the tokens). Same inputs, arithmetic and
  * errors as ispa_attn_decomp; outputs:
- *   o_full, lse_full  as in ispa_attn_decomp (either may be NULL);
+ *   o_full            as in ispa_attn_decomp, required (ISPA_ERR_NULL);
+ *   lse_full          as in ispa_attn_decomp, may be NULL;
  *   xt, dt            X = O_local and D = O_full - O_local, bf16, element
  *                     (query q, feature f = head * head_dim + j) at
  *                     [f * ld + q]: [n_heads * head_dim][ld], the same bf16
@@ -112,7 +113,8 @@ int ispa_attn_decomp(const void* q, int64_t n_q,
  *                     side by side (xt + s * n_q with a common ld) and their
  *                     statistics formed in one ispa_gram_accumulate_t call.
  * ld >= n_q (ISPA_ERR_SHAPE), ld % 8 == 0 and xt, dt 16-byte aligned
- * (ISPA_ERR_ALIGN).
+ * (ISPA_ERR_ALIGN), n_heads * head_dim * ld * 2 < 2^31 bytes
+ * (ISPA_ERR_UNSUPPORTED).
  */
 int ispa_attn_decomp_t(const void* q, int64_t n_q,
                        const void* k_sink, const void* v_sink, int64_t n_sink,

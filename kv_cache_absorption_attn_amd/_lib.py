@@ -283,11 +283,12 @@ def ispa_attn_decomp(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: 
 
 
 def ispa_attn_decomp_t(q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, sm_scale: float, xt,
-                       dt, *, col: int = 0, o_full=None, lse_full=None, stream=None) -> None:
+                       dt, *, o_full, col: int = 0, lse_full=None, stream=None) -> None:
     """The warmup step's attention with X = O_local and D written
     feature-major: xt, dt are [H*d, ld] bf16 tensors and this call fills
     their columns [col, col + n_q) (col % 8 == 0), so the warmup steps of one
-    layer can sit side by side; o_full / lse_full optional as in
+    layer can sit side by side; o_full [n_q, H*d] bf16 is required (the
+    kernel keeps X in it until the merge), lse_full optional as in
     ispa_attn_decomp."""
     n_q, n_heads, head_dim, segs, outs = _attn_args(
         q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist,

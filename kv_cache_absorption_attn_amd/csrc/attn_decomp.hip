@@ -20,14 +20,15 @@
 //   S-wave: the online softmax of tile j on S^T (each lane owns one query per
 //           block: in-lane reductions plus one exchange between the lane
 //           halves), P^T to LDS in the MFMA operand layout with the rescale
-//           factors of any move of the running max, interleaved slice by
-//           slice with S^T[64 keys x 64 queries] = K Q^T of tile j+1
-//           (32 MFMA 32x32x16, K from LDS with 16-byte reads, Q^T in
-//           registers), so the vector work runs while the matrix cores are
-//           busy.
+//           factors of any move of the running max, then S^T[64 keys x 64
+//           queries] = K Q^T of tile j+1 as one burst (32 MFMA 32x32x16, K
+//           from LDS with 16-byte reads, Q^T in registers).
 //   O-wave: O^T[d x 64 queries] = alpha O^T + V^T P^T of tile j-1 (32 MFMA,
 //           V^T by transposing LDS reads several MFMAs ahead, P^T by 16-byte
-//           reads)
+//           reads), then the loads of the next tiles.
+// The two waves of a pair share a SIMD and so take turns: the O-wave's
+// MFMAs run while the S-wave does its vector work and the reverse, without
+// either waiting on LDS writes of the tile loads.
 // Each K and V fragment read from LDS feeds two MFMAs (both query blocks).
 // The key order inside V^T is permuted so that the keys a lane holds in its
 // S^T registers are exactly the k-slots of the P^T operand.
@@ -201,35 +202,31 @@ __device__ __forceinline__ void load_o(const uint16_t* in, f32x16* o, int64_t qi
   }
 }
 
-// Feature-major forms of store_o / load_o: element (query qi, feature
+// Feature-major form of store_o: element (query qi, feature
 // head * D + d) at out[(head * D + d) * ld + qi]. Consecutive lanes hold
 // consecutive queries, so each store covers 64 contiguous bytes of two rows.
+// Buffer accesses with 32-bit byte offsets (a [h][ld] buffer stays below
+// 2^31 bytes): one offset register per access instead of a 64-bit address.
 template <int D>
 __device__ __forceinline__ void store_ot(uint16_t* out, const f32x16* o, int64_t qi, int64_t ld,
                                          int head, int hf) {
-  uint16_t* col = out + static_cast<int64_t>(head) * D * ld + qi;
+  const auto rs = raw_rsrc(out);
+  const uint32_t step = static_cast<uint32_t>(ld) * 2u;
+  const uint32_t base = static_cast<uint32_t>(head * D + 4 * hf) * step +
+                        static_cast<uint32_t>(qi) * 2u;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        col[static_cast<int64_t>(32 * db + 8 * g + 4 * hf + r) * ld] =
-            f32_to_bf16_bits(o[db][4 * g + r]);
-}
-
-template <int D>
-__device__ __forceinline__ void load_ot(const uint16_t* in, f32x16* o, int64_t qi, int64_t ld,
-                                        int head, int hf) {
-  const uint16_t* col = in + static_cast<int64_t>(head) * D * ld + qi;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        o[db][4 * g + r] =
-            bf16_bits_to_f32(col[static_cast<int64_t>(32 * db + 8 * g + 4 * hf + r) * ld]);
+        __builtin_amdgcn_raw_buffer_store_b16(
+            f32_to_bf16_bits(o[db][4 * g + r]), rs,
+            static_cast<int>(base + static_cast<uint32_t>(32 * db + 8 * g + r) * step), 0, 0);
+    // one 32-row block at a time: the conversions and offsets of all four
+    // would otherwise be formed up front, at the register peak of the kernel
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // One workgroup's work item `work` (head x query tile) of one attention call.
@@ -398,9 +395,11 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
     __syncthreads();  // every wave is done with K of tile 0 before tile 2 replaces it
 
     // Softmax of one tile (scores sc) and, when QK, K Q^T of the next tile
-    // (into sn, from K in ks). Slot u holds a slice of the softmax followed
-    // by MFMA u; the scheduling barriers keep that order, so the vector work
-    // runs while the matrix cores are busy.
+    // (into sn, from K in ks). The softmax is laid out in slots (one per MFMA
+    // of a tile's K Q^T) that fix the order of its slices; K Q^T then runs as
+    // one burst of MFMAs. The O-wave of the pair issues its P V while this
+    // wave is in the vector work, so the two waves take turns on the matrix
+    // pipe instead of interleaving MFMAs of both at every slot.
     //   row max      (8 parts: query block x 4 scores of each key half)
     //   decision     (exchange between the lane halves, lazy rescale)
     //   exponentials (16 items: query block x key step x half)
@@ -435,21 +434,18 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
         else
           return *reinterpret_cast<const bf16x8*>(ks + kf + 32 * D * half + (kx ^ (16 * t)));
       };
-      // operands of the two key halves, each read at the top of the slot two
-      // slots before its first MFMA (the register being reloaded was last
-      // read by the previous slot's MFMA)
-      KF f0, f1;
+      // K fragments of three k-steps in a ring: the first two are read before
+      // the softmax, so their LDS latency hides under it
+      KF kb[3][2];
       if constexpr (QK) {
-        f0 = kfrag(0, 0);
-        f1 = kfrag(0, 1);
+#pragma unroll
+        for (int t = 0; t < 2 && t < NT; ++t) {
+          kb[t][0] = kfrag(t, 0);
+          kb[t][1] = kfrag(t, 1);
+        }
       }
 #pragma unroll
       for (int u = 0; u < NMF; ++u) {
-        if constexpr (QK) {
-          const int t = u / 4;
-          if (u % 4 == 0 && u > 0) f1 = kfrag(t, 1);
-          if (u % 4 == 2 && t + 1 < NT) f0 = kfrag(t + 1, 0);
-        }
         // row max: one chain per query block (dependent max3 issue at full
         // rate), 8 parts of 4 scores of each key half
 #pragma unroll
@@ -507,13 +503,25 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
             l_run[qb] += lsum[qb][st];
           }
         }
-        if constexpr (QK) {
-          const int t = u / 4, kh = (u / 2) % 2, qb = u % 2;
-          if constexpr (F8)
-            sn[kh][qb] = mfma_e4m3(kh ? f1 : f0, qf8[qb][t], t ? sn[kh][qb] : f32x16{});
-          else
-            sn[kh][qb] = mfma32x32x16(kh ? f1 : f0, qf[qb][t], t ? sn[kh][qb] : f32x16{});
-          __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (QK) {
+        // K Q^T of the next tile, fragments read two k-steps ahead
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t + 2 < NT) {
+            kb[(t + 2) % 3][0] = kfrag(t + 2, 0);
+            kb[(t + 2) % 3][1] = kfrag(t + 2, 1);
+          }
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              if constexpr (F8)
+                sn[kh][qb] = mfma_e4m3(kb[t % 3][kh], qf8[qb][t], t ? sn[kh][qb] : f32x16{});
+              else
+                sn[kh][qb] = mfma32x32x16(kb[t % 3][kh], qf[qb][t], t ? sn[kh][qb] : f32x16{});
+            }
         }
       }
       if constexpr (!QK) {
@@ -627,11 +635,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
   // while the history phase runs, so D is formed against exactly that X: it
   // is parked in an output row this lane owns (O_local if requested, else
   // O_full, else D; each is written with its final value only after the
-  // parked X has been read back), or, with none of those requested, in its
-  // feature-major copy. With none of them requested, no merge is formed and
-  // X is not needed.
+  // parked X has been read back). With none of them requested, no merge is
+  // formed and X is not needed. The feature-major copies of X and D are
+  // written in the epilogue from the parked X (the entry point that asks for
+  // them always supplies O_full), which keeps their stores out of the tile
+  // loop, where the O sums hold most of the registers.
   uint16_t* const park = p.o_local ? p.o_local : (p.o_full ? p.o_full : p.d_out);
-  const bool park_t = park == nullptr && p.xt != nullptr;
   TrOff voff[NB];  // lane offsets of the V^T operand reads, per 32-wide d block
 #pragma unroll
   for (int b = 0; b < NB; ++b) voff[b] = tr_offsets<D>(32 * b, lane);
@@ -645,17 +654,22 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
     uint16_t* __restrict__ nks = BUF ? sk1 : sk0;        // K of tile it+2
     const uint4* __restrict__ sp = BUF ? sp0 : sp1;      // P of tile it-1
     const float* __restrict__ sal = BUF ? sal0 : sal1;
-    if (it < T) {
-      Seg sg;
-      int valid;
-      int64_t row0;
-      tile_of(it, sg, row0, valid);
-      loader.issue_v(sg, row0, valid, rs, nvs);
-      if (it + 2 < T) {
-        tile_of(it + 2, sg, row0, valid);
-        issue_k(sg, row0, valid, nks);
+    // the next tiles' loads go out after this step's P V: issued before it,
+    // their LDS writes compete with the V and P operand reads of the MFMAs
+    // for the LDS queues and stall them
+    auto issue_loads = [&]() __attribute__((always_inline)) {
+      if (it < T) {
+        Seg sg;
+        int valid;
+        int64_t row0;
+        tile_of(it, sg, row0, valid);
+        loader.issue_v(sg, row0, valid, rs, nvs);
+        if (it + 2 < T) {
+          tile_of(it + 2, sg, row0, valid);
+          issue_k(sg, row0, valid, nks);
+        }
       }
-    }
+    };
     if (it >= 1) {
       const int jb = it - 1;
       const float al0 = sal[prow2 + 64 * hf + l32], al1 = sal[prow2 + 64 * hf + 32 + l32];
@@ -701,15 +715,13 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
           const float inv = s_inv_loc[prow + 32 * qb + l32];
 #pragma unroll
           for (int b = 0; b < NB; ++b) oacc[qb][b] *= inv;
-          if (qvalid[qb]) {
-            if (park) store_o<D>(park, oacc[qb], qi[qb], rs, head, hf);
-            if (p.xt) store_ot<D>(p.xt, oacc[qb], qi[qb], p.ldt, head, hf);
-          }
+          if (qvalid[qb] && park) store_o<D>(park, oacc[qb], qi[qb], rs, head, hf);
 #pragma unroll
           for (int b = 0; b < NB; ++b) oacc[qb][b] = f32x16{};
         }
       }
     }
+    issue_loads();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
@@ -734,13 +746,11 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
 #pragma unroll
     for (int b = 0; b < NB; ++b) oacc[qb][b] *= inv;
     if (p.o_hist) store_o<D>(p.o_hist, oacc[qb], qi[qb], rs, head, hf);
-    if (!park && !park_t) continue;
+    if (!park) continue;
     const float w_h = s_wh[prow + 32 * qb + l32];
     f32x16 xl[NB];
-    if (park)
-      load_o<D>(park, xl, qi[qb], rs, head, hf);
-    else
-      load_ot<D>(p.xt, xl, qi[qb], p.ldt, head, hf);
+    load_o<D>(park, xl, qi[qb], rs, head, hf);
+    if (p.xt) store_ot<D>(p.xt, xl, qi[qb], p.ldt, head, hf);
 #pragma unroll
     for (int b = 0; b < NB; ++b) oacc[qb][b] = (oacc[qb][b] - xl[b]) * w_h;
     if (p.d_out) store_o<D>(p.d_out, oacc[qb], qi[qb], rs, head, hf);

@@ -301,9 +301,11 @@ int ispa_attn_decomp_t(const void* q, int64_t n_q, const void* k_sink, const voi
                        const void* k_hist, const void* v_hist, int64_t n_hist, int n_heads,
                        int head_dim, float sm_scale, void* o_full, float* lse_full, void* xt,
                        void* dt, int64_t ld, void* stream) {
-  if (!xt || !dt) return ISPA_ERR_NULL;
+  if (!xt || !dt || !o_full) return ISPA_ERR_NULL;
   if (ld < n_q || ld < 1) return ISPA_ERR_SHAPE;
   if (ld % 8 != 0) return ISPA_ERR_ALIGN;
+  // the feature-major outputs are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(n_heads) * head_dim * ld * 2 > INT32_MAX) return ISPA_ERR_UNSUPPORTED;
   ispa::AttnParams p{};
   bool run = false;
   const int st = attn_setup(q, n_q, k_sink, v_sink, n_sink, k_cur, v_cur, n_cur, k_hist, v_hist,

@@ -24,7 +24,8 @@ struct AttnParams {
   uint16_t* d_out;
   // feature-major copies of X = O_local and of D (element (query q, feature
   // f) at [f * ldt + q]), the operands of the feature-major Gram; either may
-  // be null
+  // be null, and they are written only when a token-major output holds the
+  // parked X (o_local, o_full or d_out)
   uint16_t* xt;
   uint16_t* dt;
   int64_t ldt;

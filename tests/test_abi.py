@@ -80,6 +80,8 @@ def test_feature_major_validation():
     def at(of=A, lf=0, xt=A, dt=A, ld=16):
         return L.ispa_attn_decomp_t(*seg, of, lf, xt, dt, ld, 0)
     assert at(xt=0) == NULL and at(dt=0) == NULL
+    assert at(of=0) == NULL               # O_full is required
+    assert at(ld=2 ** 22) == UNSUP        # 256 features x 2^22 tokens = 2 GiB
     assert at(ld=8) == SHAPE              # ld < n_q
     assert at(ld=20) == ALIGN             # ld % 8
     assert at(xt=MIS) == ALIGN

@@ -35,9 +35,9 @@ def custom(n_q, n_sink, n_cur, n_hist, heads, d, seed=0):
                                hist_per_step=(n_hist,), qkv_std=1.0)
 
 
-def attention_t(st, scale, ld, col, with_full=True):
+def attention_t(st, scale, ld, col):
     """ispa_attn_decomp_t into columns [col, col + n_q) of [h, ld] buffers
-    pre-filled with a sentinel; returns host X^T, D^T, O_F and the buffers."""
+    pre-filled with a sentinel; returns the X^T, D^T and O_F buffers."""
     q = dev_bf16(st.q)
     n_q, nh, d = q.shape
     kv = [dev_bf16(a) if a.shape[0] else None for a in
@@ -45,37 +45,34 @@ def attention_t(st, scale, ld, col, with_full=True):
     h = nh * d
     xt = torch.full((h, ld), 7.0, dtype=torch.bfloat16, device="cuda")
     dt = torch.full((h, ld), 7.0, dtype=torch.bfloat16, device="cuda")
-    o_full = torch.full((n_q, h), float("nan"), dtype=torch.bfloat16, device="cuda") \
-        if with_full else None
+    o_full = torch.full((n_q, h), float("nan"), dtype=torch.bfloat16, device="cuda")
     ispa.ispa_attn_decomp_t(q, *kv, scale, xt, dt, col=col, o_full=o_full)
     torch.cuda.synchronize()
     return xt, dt, o_full
 
 
-@pytest.mark.parametrize("n_q,n_sink,n_cur,n_hist,heads,d,ld,col,full",
-                         [(200, 37, 101, 301, 3, 128, 216, 8, True),
-                          (130, 64, 70, 0, 2, 128, 136, 0, True),
-                          (300, 40, 90, 200, 2, 64, 640, 320, False),
-                          (64, 32, 96, 256, 2, 64, 64, 0, True)])
-def test_attention_feature_major_outputs(n_q, n_sink, n_cur, n_hist, heads, d, ld, col, full):
+@pytest.mark.parametrize("n_q,n_sink,n_cur,n_hist,heads,d,ld,col",
+                         [(200, 37, 101, 301, 3, 128, 216, 8),
+                          (130, 64, 70, 0, 2, 128, 136, 0),
+                          (300, 40, 90, 200, 2, 64, 640, 320),
+                          (64, 32, 96, 256, 2, 64, 64, 0)])
+def test_attention_feature_major_outputs(n_q, n_sink, n_cur, n_hist, heads, d, ld, col):
     """X^T and D^T equal the token-major O_local and D transposed, bit for
     bit; O_full likewise; columns outside [col, col + n_q) are untouched; and
     all of them against the oracle. Ragged query tiles, an empty history
-    (D = 0 exactly), head_dim 64 and 128, a column offset, with and without
-    O_full (then X is parked in its feature-major copy)."""
+    (D = 0 exactly), head_dim 64 and 128, column offsets."""
     w = custom(n_q, n_sink, n_cur, n_hist, heads, d, seed=n_q + d)
-    log(f"attn feature-major n_q={n_q} hist={n_hist} d={d} ld={ld} col={col} full={full}")
+    log(f"attn feature-major n_q={n_q} hist={n_hist} d={d} ld={ld} col={col}")
     st = wl.step_inputs(w, 0, 0, q_gain=2.0)
     scale = 1.0 / np.sqrt(d)
     ref_gpu, _ = run_attention(st, scale, outputs=("o_local", "o_full", "d"))
-    xt, dt, o_full = attention_t(st, scale, ld, col, with_full=full)
+    xt, dt, o_full = attention_t(st, scale, ld, col)
     xh, dh = host(xt), host(dt)
     np.testing.assert_array_equal(xh[:, col:col + n_q].T, ref_gpu["o_local"])
     np.testing.assert_array_equal(dh[:, col:col + n_q].T, ref_gpu["d"])
     for a in (xh, dh):
         assert np.all(a[:, :col] == 7.0) and np.all(a[:, col + n_q:] == 7.0)
-    if full:
-        np.testing.assert_array_equal(host(o_full), ref_gpu["o_full"])
+    np.testing.assert_array_equal(host(o_full), ref_gpu["o_full"])
     if n_hist == 0:
         assert np.all(dh[:, col:col + n_q] == 0)
     ref = orc.decomposable_attention(st.q, st.k_sink, st.v_sink, st.k_cur, st.v_cur, st.k_hist,
@@ -147,6 +144,7 @@ def test_warmup_chain_feature_major_equals_token_major():
     ld = n * w.n_steps
     xt = torch.empty((h, ld), dtype=torch.bfloat16, device="cuda")
     dt = torch.empty_like(xt)
+    o_full = torch.empty((n, h), dtype=torch.bfloat16, device="cuda")
     G0 = torch.empty((h, h), dtype=torch.float32, device="cuda")
     C0, E0 = torch.empty_like(G0), torch.empty_like(G0)
     xs, ds = [], []
@@ -154,7 +152,8 @@ def test_warmup_chain_feature_major_equals_token_major():
         st = wl.step_inputs(w, 0, s)
         kv = [dev_bf16(a) if a.shape[0] else None for a in
               (st.k_sink, st.v_sink, st.k_cur, st.v_cur, st.k_hist, st.v_hist)]
-        ispa.ispa_attn_decomp_t(dev_bf16(st.q), *kv, w.sm_scale, xt, dt, col=s * n)
+        ispa.ispa_attn_decomp_t(dev_bf16(st.q), *kv, w.sm_scale, xt, dt, col=s * n,
+                                o_full=o_full)
         _, dev = run_attention(st, w.sm_scale, outputs=("o_local", "d"))
         ispa.ispa_gram_accumulate(dev["o_local"], dev["d"], G0, C0, E0, zero_first=(s == 0))
         xs.append(host(dev["o_local"]))
