@@ -20,15 +20,15 @@
 //   S-wave: the online softmax of tile j on S^T (each lane owns one query per
 //           block: in-lane reductions plus one exchange between the lane
 //           halves), P^T to LDS in the MFMA operand layout with the rescale
-//           factors of any move of the running max, then S^T[64 keys x 64
-//           queries] = K Q^T of tile j+1 as one burst (32 MFMA 32x32x16, K
-//           from LDS with 16-byte reads, Q^T in registers).
+//           factors of any move of the running max, interleaved slice by
+//           slice with S^T[64 keys x 64 queries] = K Q^T of tile j+1
+//           (32 MFMA 32x32x16, K from LDS with 16-byte reads, Q^T in
+//           registers), so the vector work runs while the matrix cores are
+//           busy.
 //   O-wave: O^T[d x 64 queries] = alpha O^T + V^T P^T of tile j-1 (32 MFMA,
 //           V^T by transposing LDS reads several MFMAs ahead, P^T by 16-byte
-//           reads), then the loads of the next tiles.
-// The two waves of a pair share a SIMD and so take turns: the O-wave's
-// MFMAs run while the S-wave does its vector work and the reverse, without
-// either waiting on LDS writes of the tile loads.
+//           reads), then the loads of the next tiles, issued after P V so
+//           that their LDS writes do not hold up its operand reads.
 // Each K and V fragment read from LDS feeds two MFMAs (both query blocks).
 // The key order inside V^T is permuted so that the keys a lane holds in its
 // S^T registers are exactly the k-slots of the P^T operand.
@@ -395,11 +395,9 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
     __syncthreads();  // every wave is done with K of tile 0 before tile 2 replaces it
 
     // Softmax of one tile (scores sc) and, when QK, K Q^T of the next tile
-    // (into sn, from K in ks). The softmax is laid out in slots (one per MFMA
-    // of a tile's K Q^T) that fix the order of its slices; K Q^T then runs as
-    // one burst of MFMAs. The O-wave of the pair issues its P V while this
-    // wave is in the vector work, so the two waves take turns on the matrix
-    // pipe instead of interleaving MFMAs of both at every slot.
+    // (into sn, from K in ks). Slot u holds a slice of the softmax followed
+    // by MFMA u; the scheduling barriers keep that order, so the vector work
+    // runs while the matrix cores are busy.
     //   row max      (8 parts: query block x 4 scores of each key half)
     //   decision     (exchange between the lane halves, lazy rescale)
     //   exponentials (16 items: query block x key step x half)
@@ -434,18 +432,21 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
         else
           return *reinterpret_cast<const bf16x8*>(ks + kf + 32 * D * half + (kx ^ (16 * t)));
       };
-      // K fragments of three k-steps in a ring: the first two are read before
-      // the softmax, so their LDS latency hides under it
-      KF kb[3][2];
+      // operands of the two key halves, each read at the top of the slot two
+      // slots before its first MFMA (the register being reloaded was last
+      // read by the previous slot's MFMA)
+      KF f0, f1;
       if constexpr (QK) {
-#pragma unroll
-        for (int t = 0; t < 2 && t < NT; ++t) {
-          kb[t][0] = kfrag(t, 0);
-          kb[t][1] = kfrag(t, 1);
-        }
+        f0 = kfrag(0, 0);
+        f1 = kfrag(0, 1);
       }
 #pragma unroll
       for (int u = 0; u < NMF; ++u) {
+        if constexpr (QK) {
+          const int t = u / 4;
+          if (u % 4 == 0 && u > 0) f1 = kfrag(t, 1);
+          if (u % 4 == 2 && t + 1 < NT) f0 = kfrag(t + 1, 0);
+        }
         // row max: one chain per query block (dependent max3 issue at full
         // rate), 8 parts of 4 scores of each key half
 #pragma unroll
@@ -503,25 +504,13 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
             l_run[qb] += lsum[qb][st];
           }
         }
-      }
-      if constexpr (QK) {
-        // K Q^T of the next tile, fragments read two k-steps ahead
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (t + 2 < NT) {
-            kb[(t + 2) % 3][0] = kfrag(t + 2, 0);
-            kb[(t + 2) % 3][1] = kfrag(t + 2, 1);
-          }
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              if constexpr (F8)
-                sn[kh][qb] = mfma_e4m3(kb[t % 3][kh], qf8[qb][t], t ? sn[kh][qb] : f32x16{});
-              else
-                sn[kh][qb] = mfma32x32x16(kb[t % 3][kh], qf[qb][t], t ? sn[kh][qb] : f32x16{});
-            }
+        if constexpr (QK) {
+          const int t = u / 4, kh = (u / 2) % 2, qb = u % 2;
+          if constexpr (F8)
+            sn[kh][qb] = mfma_e4m3(kh ? f1 : f0, qf8[qb][t], t ? sn[kh][qb] : f32x16{});
+          else
+            sn[kh][qb] = mfma32x32x16(kh ? f1 : f0, qf[qb][t], t ? sn[kh][qb] : f32x16{});
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       if constexpr (!QK) {
