@@ -416,6 +416,12 @@ int ispa_project_w8a8_noalloc(const void* x, const void* wq, const float* w_scal
  *   above the diagonal) and ref [n_layers] fp64 is computed. info as for
  *   ispa_ridge_solve (linv and ref are meaningless where info != 0).
  *   workspace: ispa_ridge_workspace_bytes(n_layers, h) bytes at least.
+ * ispa_drift_prepare_factored: the same linv and ref from the factor that the
+ *   preceding ispa_ridge_solve(n_layers, h, G, ..., lambda, ...) left in its
+ *   workspace, without factoring M again. The workspace must be that call's,
+ *   on the same stream, with no ispa_layer_score (which reuses the factor's
+ *   storage) or other call on it in between; the failure flags are that
+ *   call's info. Bit-identical to ispa_drift_prepare on the same G and lambda.
  * ispa_drift_score: x [n_layers][n_tok, h] bf16; the sample is the rows
  *   0, stride, 2 stride, ... (ceil(n_tok / stride) of them); score
  *   [n_layers] fp64 out (+inf when ref is 0); ref and score need only
@@ -430,6 +436,9 @@ size_t ispa_drift_workspace_bytes(int n_layers, int h, int64_t n_sample);
 int ispa_drift_prepare(int n_layers, int h, const float* G, float lambda,
                        int64_t n_warm, float* linv, double* ref, int* info,
                        void* workspace, size_t ws_bytes, void* stream);
+int ispa_drift_prepare_factored(int n_layers, int h, float lambda, int64_t n_warm,
+                                float* linv, double* ref, void* workspace, size_t ws_bytes,
+                                void* stream);
 int ispa_drift_score(int n_layers, int h, const float* linv, const double* ref,
                      const void* x, int64_t n_tok, int64_t stride, double* score,
                      void* workspace, size_t ws_bytes, void* stream);

@@ -9,7 +9,7 @@ binding plus the warmup / streaming drivers built on it.
 from ._lib import (EXPORTED, SESSION_FP8_ATTN, SESSION_W8A8, IspaError, KVCache, KVView,
                    Session, SessionConfig, SessionState,
                    ispa_apply_dW, ispa_attn_decomp, ispa_attn_decomp_t, ispa_drift_prepare,
-                   ispa_drift_score, ispa_gram_accumulate_t,
+                   ispa_drift_prepare_factored, ispa_drift_score, ispa_gram_accumulate_t,
                    ispa_drift_workspace_bytes, ispa_gram_accumulate, ispa_layer_score,
                    ispa_project, ispa_project_w8a8, ispa_project_w8a8_noalloc,
                    ispa_project_w8a8_workspace_bytes,
@@ -20,7 +20,8 @@ from ._lib import (EXPORTED, SESSION_FP8_ATTN, SESSION_W8A8, IspaError, KVCache,
 
 __all__ = ["SESSION_W8A8", "SESSION_FP8_ATTN", "IspaError", "KVCache", "KVView", "Session",
            "SessionConfig", "SessionState",
-           "ispa_drift_prepare", "ispa_drift_score", "ispa_drift_workspace_bytes",
+           "ispa_drift_prepare", "ispa_drift_prepare_factored", "ispa_drift_score",
+           "ispa_drift_workspace_bytes",
            "ispa_quantize_fp8", "ispa_project_w8a8", "ispa_project_w8a8_noalloc",
            "ispa_project_w8a8_workspace_bytes",
            "ispa_attn_decomp_fp8", "ispa_attn_fp8_workspace_bytes", "ispa_key_mean",

@@ -136,6 +136,8 @@ lib.ispa_drift_workspace_bytes.restype = _sz
 lib.ispa_drift_workspace_bytes.argtypes = [_i, _i, _i64]
 lib.ispa_drift_prepare.restype = _i
 lib.ispa_drift_prepare.argtypes = [_i, _i, _p, _f, _i64, _p, _p, _p, _p, _sz, _p]
+lib.ispa_drift_prepare_factored.restype = _i
+lib.ispa_drift_prepare_factored.argtypes = [_i, _i, _f, _i64, _p, _p, _p, _sz, _p]
 lib.ispa_drift_score.restype = _i
 lib.ispa_drift_score.argtypes = [_i, _i, _p, _p, _p, _i64, _i64, _p, _p, _sz, _p]
 
@@ -196,7 +198,7 @@ EXPORTED = ("ispa_status_string", "ispa_version", "ispa_attn_decomp", "ispa_gram
             "ispa_kv_view_of", "ispa_kv_write", "ispa_kv_advance", "ispa_kv_evict_history",
             "ispa_kv_last_error", "ispa_kv_resident_bytes", "ispa_kv_attn",
             "ispa_kv_layer_forward", "ispa_kv_restore_history", "ispa_drift_workspace_bytes",
-            "ispa_drift_prepare", "ispa_drift_score", "ispa_session_workspace_bytes",
+            "ispa_drift_prepare", "ispa_drift_prepare_factored", "ispa_drift_score", "ispa_session_workspace_bytes",
             "ispa_session_create", "ispa_session_destroy", "ispa_session_cache",
             "ispa_session_layer", "ispa_session_end_chunk", "ispa_session_query",
             "ispa_quantize_fp8", "ispa_project_w8a8_workspace_bytes", "ispa_project_w8a8",
@@ -612,6 +614,22 @@ def ispa_drift_prepare(G, lam: float, n_warm: int, linv, ref, info, workspace, *
                                 _ptr(workspace, None, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ispa_drift_prepare", st)
+
+
+def ispa_drift_prepare_factored(n_layers: int, h: int, lam: float, n_warm: int, linv, ref,
+                                ridge_workspace, *, stream=None) -> None:
+    """linv and ref as ispa_drift_prepare gives them, from the factor the
+    preceding ispa_ridge_solve left in ridge_workspace (same G and lambda,
+    nothing else run on that workspace in between)."""
+    if tuple(linv.shape) != (n_layers, h, h) or ref.shape[0] != n_layers:
+        raise ValueError("ispa_drift_prepare_factored: shape mismatch")
+    st = lib.ispa_drift_prepare_factored(n_layers, h, float(lam), int(n_warm),
+                                         _ptr(linv, torch.float32, "linv"),
+                                         _ptr(ref, torch.float64, "ref"),
+                                         _ptr(ridge_workspace, None, "workspace"),
+                                         ridge_workspace.numel() * ridge_workspace.element_size(),
+                                         _stream(stream))
+    _check("ispa_drift_prepare_factored", st)
 
 
 def ispa_drift_score(linv, ref, x, stride: int, score, workspace, *, stream=None) -> None:

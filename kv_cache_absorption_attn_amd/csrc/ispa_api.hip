@@ -656,6 +656,28 @@ int ispa_drift_prepare(int n_layers, int h, const float* G, float lambda, int64_
   return ISPA_OK;
 }
 
+int ispa_drift_prepare_factored(int n_layers, int h, float lambda, int64_t n_warm, float* linv,
+                                double* ref, void* workspace, size_t ws_bytes, void* stream) {
+  if (!linv || !ref || !workspace) return ISPA_ERR_NULL;
+  if (n_layers < 1 || h < 1 || n_warm < 1 || !(lambda >= 0.f) || !isfinite(lambda))
+    return ISPA_ERR_SHAPE;
+  if (h % 8 != 0) return ISPA_ERR_UNSUPPORTED;
+  if (ws_bytes < ridge_layout(nullptr, n_layers, h).bytes) return ISPA_ERR_WORKSPACE;
+  if (!aligned16(linv) || !aligned16(ref) || !aligned16(workspace)) return ISPA_ERR_ALIGN;
+  // the factor and its diagonal-block inverses are where ispa_ridge_solve
+  // left them; only the forward solve L Z = I and the trace remain
+  RidgeWs w = ridge_layout(workspace, n_layers, h);
+  w.R = linv;
+  const hipStream_t s = as_stream(stream);
+  const int nblk = (h + kCholBlock - 1) / kCholBlock;
+  const int64_t hh = static_cast<int64_t>(h) * h;
+  ISPA_TRY(ispa::launch_identity(linv, h, n_layers, s));
+  ISPA_TRY(solve_lower(0, nblk, w, w.R, h, n_layers, s));
+  ISPA_TRY(ispa::launch_drift_sum(linv, h, h, h, hh, n_layers, w.part, h, lambda,
+                                  static_cast<double>(n_warm), nullptr, ref, s));
+  return ISPA_OK;
+}
+
 int ispa_drift_score(int n_layers, int h, const float* linv, const double* ref, const void* x,
                      int64_t n_tok, int64_t stride, double* score, void* workspace,
                      size_t ws_bytes, void* stream) {

@@ -43,7 +43,7 @@ struct Layout {
   void* drift_ws;
   size_t drift_bytes;
   uint16_t *x, *d, *o;
-  int *info, *info_drift, *selected;
+  int *info, *selected;
   double *eps_abs, *eps_rel, *ref, *score;
   // quantized variant (present only with the matching flag)
   uint8_t* wq;           // [n_layers][h, h] E4M3 codes of the active weights
@@ -88,7 +88,6 @@ Layout layout(const ispa_session_config& c, void* base) {
   w.d = reinterpret_cast<uint16_t*>(take(act));
   w.o = reinterpret_cast<uint16_t*>(take(act));
   w.info = reinterpret_cast<int*>(take(L * sizeof(int)));
-  w.info_drift = reinterpret_cast<int*>(take(L * sizeof(int)));
   w.selected = reinterpret_cast<int*>(take(L * sizeof(int)));
   w.eps_abs = reinterpret_cast<double*>(take(L * sizeof(double)));
   w.eps_rel = reinterpret_cast<double*>(take(L * sizeof(double)));
@@ -372,6 +371,11 @@ int ispa_session_end_chunk(ispa_session* s, void* stream, int* event) {
     // transition: solve against the original W, score, select, update
     st = ispa_ridge_solve(L, s->h, s->ws.G, s->ws.C, s->wo, c.lambda, s->ws.dW, s->ws.info,
                           s->ws.ridge_ws, s->ws.ridge_bytes, stream);
+    // the drift reference from the ridge's own factor of G + lambda I, before
+    // the score reuses its storage
+    if (st == ISPA_OK && c.drift_threshold > 0.0)
+      st = ispa_drift_prepare_factored(L, s->h, c.lambda, c.n_cur * c.t_warm, s->ws.linv,
+                                       s->ws.ref, s->ws.ridge_ws, s->ws.ridge_bytes, stream);
     if (st == ISPA_OK)
       st = ispa_layer_score(L, s->h, s->ws.G, s->ws.C, s->ws.E, s->wo, s->ws.dW, c.lambda,
                             s->ws.info, c.k_select, s->ws.ridge_ws, s->ws.ridge_bytes,
@@ -381,10 +385,6 @@ int ispa_session_end_chunk(ispa_session* s, void* stream, int* event) {
       st = ISPA_ERR_HIP;
     if (st == ISPA_OK) st = ispa_apply_dW(L, s->h, s->ws.selected, s->ws.dW, s->w, stream);
     if (st == ISPA_OK) st = requantize(s, stream);
-    if (st == ISPA_OK && c.drift_threshold > 0.0)
-      st = ispa_drift_prepare(L, s->h, s->ws.G, c.lambda, c.n_cur * c.t_warm, s->ws.linv,
-                              s->ws.ref, s->ws.info_drift, s->ws.ridge_ws, s->ws.ridge_bytes,
-                              stream);
     if (st != ISPA_OK) return st;
     // which layers turn local is a host decision: their history is freed
     std::vector<int> sel(L);

@@ -295,6 +295,16 @@ def test_drift_and_session_validation():
     assert L.ispa_drift_prepare(2, 100, A, 0.01, 10, A, A, A, A, need, 0) == UNSUP
     assert L.ispa_drift_prepare(2, 128, A, 0.01, 10, A, A, A, A, 64, 0) == WS
     assert L.ispa_drift_prepare(2, 128, MIS, 0.01, 10, A, A, A, A, need, 0) == ALIGN
+    rneed = ispa.ispa_ridge_workspace_bytes(2, 128)
+    pf = L.ispa_drift_prepare_factored
+    assert pf(2, 128, 0.01, 10, 0, A, A, rneed, 0) == NULL
+    assert pf(2, 128, 0.01, 10, A, A, 0, rneed, 0) == NULL
+    assert pf(0, 128, 0.01, 10, A, A, A, rneed, 0) == SHAPE
+    assert pf(2, 128, float("inf"), 10, A, A, A, rneed, 0) == SHAPE
+    assert pf(2, 128, 0.01, 0, A, A, A, rneed, 0) == SHAPE
+    assert pf(2, 100, 0.01, 10, A, A, A, rneed, 0) == UNSUP
+    assert pf(2, 128, 0.01, 10, A, A, A, rneed - 1, 0) == WS
+    assert pf(2, 128, 0.01, 10, A, MIS, A, rneed, 0) == ALIGN
     assert L.ispa_drift_score(2, 128, A, A, 0, 16, 1, A, A, need, 0) == NULL
     assert L.ispa_drift_score(2, 128, A, A, A, 0, 1, A, A, need, 0) == SHAPE
     assert L.ispa_drift_score(2, 128, A, A, A, 16, 0, A, A, need, 0) == SHAPE

@@ -57,6 +57,18 @@ def test_drift_prepare_and_score(h, n_warm):
     assert abs(float(ref[0]) - ref_o) <= 1e-4 * ref_o
     li = host(linv[0])
     assert np.count_nonzero(np.triu(li, 1)) == 0
+    # the same from the factor a ridge solve on G leaves in its workspace
+    rws = torch.empty(ispa.ispa_ridge_workspace_bytes(1, h), dtype=torch.uint8, device="cuda")
+    wo = dev_bf16(wl.random_bf16((1, h, h), 0.02, 76))
+    dw = torch.empty((1, h, h), dtype=torch.float32, device="cuda")
+    rinfo = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    ispa.ispa_ridge_solve(G, torch.zeros_like(G), wo, lam, dw, rinfo, rws)
+    linv_f = torch.full_like(linv, float("nan"))
+    ref_f = torch.empty_like(ref)
+    ispa.ispa_drift_prepare_factored(1, h, lam, n_warm, linv_f, ref_f, rws)
+    torch.cuda.synchronize()
+    assert int(rinfo[0]) == 0
+    assert torch.equal(linv_f, linv) and torch.equal(ref_f, ref)
     same = wl.random_bf16((n_tok, h), 0.3, 73) @ rng_basis
     spike = wl.random_bf16((n_tok, 1), 2.0, 74) * wl.random_bf16((1, h), 1.0, 75)
     probes = {"same": same, "scaled": 3.0 * same, "new direction": same + spike}
