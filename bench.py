@@ -746,14 +746,14 @@ def trace_summary(trace_csv: str, w: wl.Workload, passes: int):
                      f"average {avg / 1e3:.1f} us for {gf / 1e9:.1f} GFLOP = "
                      f"{gf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
     proj = [dt for _, n, dt in rows
-            if "nt_gemm256_kernel<false, false>" in n or "g256_kernel<0>" in n]
+            if "nt_gemm256_kernel<false, false>" in n or "g256_kernel<0," in n]
     if proj:
         avg = sum(proj) / len(proj)
         pf = 2.0 * w.n_q * w.hidden * w.hidden
         lines.append(f"Output projections (post-absorption chunk): {len(proj)}, average "
                      f"{avg / 1e3:.1f} us for {pf / 1e9:.1f} GFLOP = "
                      f"{pf / (avg * 1e-9) / 1e12:.1f} TFLOP/s.")
-    cw = [dt for _, n, dt in rows if "g256_kernel<1>" in n]
+    cw = [dt for _, n, dt in rows if "g256_kernel<1," in n]
     if cw:
         avg = sum(cw) / len(cw)
         cf = 2.0 * 2.0 * w.n_layers * w.hidden ** 3  # two bf16 planes of the fp32 operand
