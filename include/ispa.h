@@ -255,12 +255,15 @@ int ispa_gram_accumulate_t(const void* xt, const void* dt, int64_t n_tok, int64_
  *   dW = argmin ||X (W + dW) - Z W||_F^2 + lambda ||dW||_F^2
  *      = (G + lambda I)^{-1} C W        (W = Wo^T, math layout [in, out]),
  * computed as Y = (G + lambda I)^{-1} C by a blocked fp32 Cholesky
- * factorisation of G + lambda I and two triangular solves, refined once with
- * a residual C - (G + lambda I) Y accumulated in fp64 and solved with the same
- * factor, then dW = Y W. The refinement keeps dW at the fp64 solution of the
- * given fp32 statistics to ~1e-5 relative up to cond(G + lambda I) ~ 1e5
- * (rank-deficient statistics have cond ~ ||G|| / lambda). lambda is added
- * unscaled to the summed statistics.
+ * factorisation of G + lambda I and two triangular solves, then dW = Y W.
+ * A layer whose fp32 solution may be off by more than 1e-4 relative in dW is
+ * refined once: the residual C - (G + lambda I) Y accumulated in fp64, solved
+ * with the same factor and added to Y. Which layers: the error of dW along 8
+ * fixed pseudo-random directions, from the same fp64 residual and factor
+ * applied to those directions only. Refined or not, dW is then within ~1e-4
+ * of the fp64 solution of the given fp32 statistics up to
+ * cond(G + lambda I) ~ 1e5 (rank-deficient statistics have
+ * cond ~ ||G|| / lambda). lambda is added unscaled to the summed statistics.
  * G, C     [n_layers][h, h] fp32 (read only).
  * Wo       [n_layers][h, h] bf16, nn.Linear layout (read only).
  * dW       [n_layers][h, h] fp32 output, nn.Linear layout (like Wo).
@@ -283,8 +286,8 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C,
  * tokens:
  *   eps_abs = ||X (W + dW) - Z W||_F^2
  *           = tr(W^T E W) - tr(dW^T C W) - lambda ||dW||_F^2  (at the ridge
- *             optimum, which the refined solve of ispa_ridge_solve reaches
- *             to fp32 rounding), Z = X + D, clamped at 0 (a near-exact fit
+ *             optimum, which the solve of ispa_ridge_solve reaches to ~1e-4
+ *             relative or better), Z = X + D, clamped at 0 (a near-exact fit
  *             can come out below 0 by the fp32 rounding of the traces,
  *             ~2^-24 sqrt(h) of ||Z W||^2),
  *   eps_rel = eps_abs / ||Z W||_F^2, ||Z W||^2 = tr(W^T (G + C + C^T + E) W);

@@ -110,6 +110,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(const GemmF32Para
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   if (p.tri && tm < tn) return;
   const int b = blockIdx.y;
+  if (p.layer_mask && !p.layer_mask[b]) return;
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, l32 = lane % 32, hf = lane / 32;
   const int wm = wave / 2, wn = wave % 2;
@@ -210,6 +211,7 @@ __global__ __launch_bounds__(kThreads, 2) void ridge_resid_f64_kernel(const Ridg
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int64_t hh = static_cast<int64_t>(h) * h;
   const int64_t b = blockIdx.y;
+  if (p.layer_mask && !p.layer_mask[b]) return;
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, l16 = lane % 16, q = lane / 16;
   const int wm = wave / 2, wn = wave % 2;

@@ -12,6 +12,10 @@ namespace {
 
 using ispa::kCholBlock;
 
+// Relative error of dW0 = Y0 W (the fp32 solve) above which a layer's solve
+// is refined: a tenth of the 1e-3 to which dW is held.
+constexpr double kRefineTol = 1e-4;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -33,6 +37,12 @@ struct RidgeWs {
   float* Bt;      // [n_layers][h, h] (C W)^T in nn.Linear layout
   float* Linv;    // [n_layers][h, 128] inverses of the diagonal blocks
   double* part;   // layer-score partial sums
+  int* refine;    // [n_layers] 1 where the solve is refined
+  double* pq;     // [n_layers][h, 8] probe columns W z (the refinement estimate)
+  double* pa;     // [n_layers][h, 8] C W z
+  double* pb;     // [n_layers][h, 8] Y0 W z
+  double* pt;     // [n_layers][h, 8] G Y0 W z
+  float* pe;      // [n_layers][h, 8] residual, then the error estimate
   size_t bytes;
 };
 
@@ -49,6 +59,13 @@ RidgeWs ridge_layout(void* base, int n_layers, int h) {
   w.Bt = reinterpret_cast<float*>(p + off);   off = align_up(off + hh);
   w.Linv = reinterpret_cast<float*>(p + off); off = align_up(off + lin);
   w.part = reinterpret_cast<double*>(p + off); off = align_up(off + part);
+  w.refine = reinterpret_cast<int*>(p + off);  off = align_up(off + n_layers * sizeof(int));
+  const size_t probe = static_cast<size_t>(h) * 8 * n_layers;
+  w.pq = reinterpret_cast<double*>(p + off); off = align_up(off + probe * sizeof(double));
+  w.pa = reinterpret_cast<double*>(p + off); off = align_up(off + probe * sizeof(double));
+  w.pb = reinterpret_cast<double*>(p + off); off = align_up(off + probe * sizeof(double));
+  w.pt = reinterpret_cast<double*>(p + off); off = align_up(off + probe * sizeof(double));
+  w.pe = reinterpret_cast<float*>(p + off);  off = align_up(off + probe * sizeof(float));
   w.bytes = off;
   return w;
 }
@@ -57,64 +74,77 @@ RidgeWs ridge_layout(void* base, int n_layers, int h) {
 hipError_t gemm(int M, int N, int K, const void* A, int64_t a_s0, int64_t a_s1, int64_t a_batch,
                 bool a_bf16, const void* B, int64_t b_s0, int64_t b_s1, int64_t b_batch,
                 bool b_bf16, float* C, int64_t ldc, int64_t c_batch, float alpha, float beta,
-                int batch, bool tri, hipStream_t s) {
+                int batch, bool tri, hipStream_t s, const int* mask = nullptr) {
   ispa::GemmF32Params p{};
   p.M = M; p.N = N; p.K = K;
   p.A = A; p.a_s0 = a_s0; p.a_s1 = a_s1; p.a_batch = a_batch; p.a_bf16 = a_bf16;
   p.B = B; p.b_s0 = b_s0; p.b_s1 = b_s1; p.b_batch = b_batch; p.b_bf16 = b_bf16;
   p.Cm = C; p.ldc = ldc; p.c_batch = c_batch;
   p.alpha = alpha; p.beta = beta; p.batch = batch; p.tri = tri ? 1 : 0;
+  p.layer_mask = mask;
   return ispa::launch_gemm_f32(p, s);
 }
 
 // Block rows [ba, bb) of R (128 rows per block, the last one possibly short).
 inline int blk_row(int b, int h) { return b * kCholBlock < h ? b * kCholBlock : h; }
 
-// R[rows of blocks ba..bb) <- L^-1 R for the lower-triangular factor in w.L
-// (R: h x h right-hand sides of each layer, overwritten by the solution).
-hipError_t solve_lower(int ba, int bb, const RidgeWs& w, float* R, int h, int L, hipStream_t s) {
+// Right-hand sides of the triangular solves: per layer an h x nc fp32 matrix
+// (row stride nc) at R + layer * stride; layers whose mask entry is 0 are
+// left untouched (no mask: all layers).
+struct Rhs {
+  float* R;
+  int nc;
+  int64_t stride;
+  const int* mask;
+};
+
+// Rows of blocks [ba, bb) of the right-hand sides <- L^-1 R for the
+// lower-triangular factor in w.L.
+hipError_t solve_lower(int ba, int bb, const RidgeWs& w, const Rhs& r, int h, int L,
+                       hipStream_t s) {
   const int64_t hh = static_cast<int64_t>(h) * h;
   const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
   const int r0 = blk_row(ba, h), r2 = blk_row(bb, h);
   if (bb - ba == 1) {
-    float* rk = R + static_cast<int64_t>(r0) * h;
+    float* rk = r.R + static_cast<int64_t>(r0) * r.nc;
     const float* linv = w.Linv + static_cast<int64_t>(r0) * kCholBlock;
     const int nbk = r2 - r0;
-    return gemm(nbk, h, nbk, linv, kCholBlock, 1, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
-                0.f, L, false, s);
+    return gemm(nbk, r.nc, nbk, linv, kCholBlock, 1, lb, false, rk, r.nc, 1, r.stride, false, rk,
+                r.nc, r.stride, 1.f, 0.f, L, false, s, r.mask);
   }
   const int bm = (ba + bb) / 2, r1 = blk_row(bm, h);
-  hipError_t e = solve_lower(ba, bm, w, R, h, L, s);
+  hipError_t e = solve_lower(ba, bm, w, r, h, L, s);
   if (e != hipSuccess) return e;
   // R[r1:r2] -= L[r1:r2, r0:r1] R[r0:r1]
-  e = gemm(r2 - r1, h, r1 - r0, w.L + static_cast<int64_t>(r1) * h + r0, h, 1, hh, false,
-           R + static_cast<int64_t>(r0) * h, h, 1, hh, false, R + static_cast<int64_t>(r1) * h,
-           h, hh, -1.f, 1.f, L, false, s);
+  e = gemm(r2 - r1, r.nc, r1 - r0, w.L + static_cast<int64_t>(r1) * h + r0, h, 1, hh, false,
+           r.R + static_cast<int64_t>(r0) * r.nc, r.nc, 1, r.stride, false,
+           r.R + static_cast<int64_t>(r1) * r.nc, r.nc, r.stride, -1.f, 1.f, L, false, s, r.mask);
   if (e != hipSuccess) return e;
-  return solve_lower(bm, bb, w, R, h, L, s);
+  return solve_lower(bm, bb, w, r, h, L, s);
 }
 
-// R[rows of blocks ba..bb) <- L^-T R.
-hipError_t solve_upper(int ba, int bb, const RidgeWs& w, float* R, int h, int L, hipStream_t s) {
+// Rows of blocks [ba, bb) of the right-hand sides <- L^-T R.
+hipError_t solve_upper(int ba, int bb, const RidgeWs& w, const Rhs& r, int h, int L,
+                       hipStream_t s) {
   const int64_t hh = static_cast<int64_t>(h) * h;
   const int64_t lb = static_cast<int64_t>(h) * kCholBlock;
   const int r0 = blk_row(ba, h), r2 = blk_row(bb, h);
   if (bb - ba == 1) {
-    float* rk = R + static_cast<int64_t>(r0) * h;
+    float* rk = r.R + static_cast<int64_t>(r0) * r.nc;
     const float* linv = w.Linv + static_cast<int64_t>(r0) * kCholBlock;
     const int nbk = r2 - r0;
-    return gemm(nbk, h, nbk, linv, 1, kCholBlock, lb, false, rk, h, 1, hh, false, rk, h, hh, 1.f,
-                0.f, L, false, s);
+    return gemm(nbk, r.nc, nbk, linv, 1, kCholBlock, lb, false, rk, r.nc, 1, r.stride, false, rk,
+                r.nc, r.stride, 1.f, 0.f, L, false, s, r.mask);
   }
   const int bm = (ba + bb) / 2, r1 = blk_row(bm, h);
-  hipError_t e = solve_upper(bm, bb, w, R, h, L, s);
+  hipError_t e = solve_upper(bm, bb, w, r, h, L, s);
   if (e != hipSuccess) return e;
   // R[r0:r1] -= L[r1:r2, r0:r1]^T R[r1:r2]
-  e = gemm(r1 - r0, h, r2 - r1, w.L + static_cast<int64_t>(r1) * h + r0, 1, h, hh, false,
-           R + static_cast<int64_t>(r1) * h, h, 1, hh, false, R + static_cast<int64_t>(r0) * h,
-           h, hh, -1.f, 1.f, L, false, s);
+  e = gemm(r1 - r0, r.nc, r2 - r1, w.L + static_cast<int64_t>(r1) * h + r0, 1, h, hh, false,
+           r.R + static_cast<int64_t>(r1) * r.nc, r.nc, 1, r.stride, false,
+           r.R + static_cast<int64_t>(r0) * r.nc, r.nc, r.stride, -1.f, 1.f, L, false, s, r.mask);
   if (e != hipSuccess) return e;
-  return solve_upper(ba, bm, w, R, h, L, s);
+  return solve_upper(ba, bm, w, r, h, L, s);
 }
 
 // Columns of blocks [ca, cb) of the rows [x0, x1) of w.L: X <- X L^-T for the
@@ -512,19 +542,38 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const 
   // are large.
   ISPA_TRY(hipMemcpyAsync(w.R, C, static_cast<size_t>(L) * hh * sizeof(float),
                           hipMemcpyDeviceToDevice, s));
-  ISPA_TRY(solve_lower(0, nblk, w, w.R, h, L, s));
-  ISPA_TRY(solve_upper(0, nblk, w, w.R, h, L, s));
+  const Rhs ry{w.R, h, hh, nullptr};
+  ISPA_TRY(solve_lower(0, nblk, w, ry, h, L, s));
+  ISPA_TRY(solve_upper(0, nblk, w, ry, h, L, s));
 
-  // One step of iterative refinement: the residual S = C - (G + lambda I) Y0
-  // accumulated in fp64, the correction (G + lambda I)^-1 S from the same
-  // factor, Y = Y0 + correction. The fp32 factor solves to about cond * 2^-24
-  // (1e-3 relative at cond 2e4, rank-deficient statistics: eigenvalues lambda
-  // outside the span of the warmup tokens); with the fp64 residual one step
-  // brings that to about (cond * 2^-24)^2. The system is solved for
-  // (G + lambda I)^-1 C rather than for dW directly, so that its right-hand
-  // side C is an exact input: C W formed in fp32 would carry a rounding of
-  // 2^-24 |C| |W| that no refinement of the solve can remove, and the
-  // multiplication by W after the solve is well conditioned.
+  // Iterative refinement, one step, for the layers that need it. The fp32
+  // factor solves to about cond * 2^-24 (1e-3 relative at cond 2e4,
+  // rank-deficient statistics: eigenvalues lambda outside the span of the
+  // warmup tokens). The system is solved for (G + lambda I)^-1 C rather than
+  // for dW directly, so that its right-hand side C is an exact input: C W
+  // formed in fp32 would carry a rounding of 2^-24 |C| |W| that no
+  // refinement of the solve can remove, and the multiplication by W after the
+  // solve is well conditioned.
+  //
+  // Which layers: the error of dW0 = Y0 W along 8 random directions,
+  // E W z = (G + lambda I)^-1 (C W z - (G + lambda I) Y0 W z), with the
+  // residual accumulated in fp64 and solved with the same factor; for
+  // Gaussian-like z its squared norm estimates ||E W||_F^2. A layer is refined
+  // unless that estimate is below kRefineTol relative to ||Y0 W z||. Cost:
+  // three fp64 matrix-vector passes and one 8-column solve per layer.
+  ISPA_TRY(ispa::launch_probe_wz(static_cast<const uint16_t*>(Wo), w.pq, h, L, s));
+  ISPA_TRY(ispa::launch_mv8_f64(C, w.pq, w.pa, h, L, s));
+  ISPA_TRY(ispa::launch_mv8_f64(w.R, w.pq, w.pb, h, L, s));
+  ISPA_TRY(ispa::launch_mv8_f64(G, w.pb, w.pt, h, L, s));
+  ISPA_TRY(ispa::launch_probe_resid(w.pa, w.pt, w.pb, static_cast<double>(lambda), w.pe, h, L, s));
+  const Rhs rp8{w.pe, 8, static_cast<int64_t>(h) * 8, nullptr};
+  ISPA_TRY(solve_lower(0, nblk, w, rp8, h, L, s));
+  ISPA_TRY(solve_upper(0, nblk, w, rp8, h, L, s));
+  ISPA_TRY(ispa::launch_probe_flag(w.pe, w.pb, kRefineTol, w.refine, h, L, s));
+
+  // The step: the residual S = C - (G + lambda I) Y0 accumulated in fp64,
+  // the correction (G + lambda I)^-1 S from the same factor, Y = Y0 +
+  // correction: about (cond * 2^-24)^2. Layers not flagged skip all three.
   {
     ispa::RidgeResidParams rp{};
     rp.h = h;
@@ -534,11 +583,13 @@ int ispa_ridge_solve(int n_layers, int h, const float* G, const float* C, const 
     rp.Y = w.R;
     rp.S = w.S;
     rp.lam = static_cast<double>(lambda);
+    rp.layer_mask = w.refine;
     ISPA_TRY(ispa::launch_ridge_resid_f64(rp, s));
   }
-  ISPA_TRY(solve_lower(0, nblk, w, w.S, h, L, s));
-  ISPA_TRY(solve_upper(0, nblk, w, w.S, h, L, s));
-  ISPA_TRY(ispa::launch_add_inplace(w.R, w.S, static_cast<int64_t>(L) * hh, s));
+  const Rhs rs{w.S, h, hh, w.refine};
+  ISPA_TRY(solve_lower(0, nblk, w, rs, h, L, s));
+  ISPA_TRY(solve_upper(0, nblk, w, rs, h, L, s));
+  ISPA_TRY(ispa::launch_add_inplace(w.R, w.S, hh, L, w.refine, s));
 
   // dW (math layout [in, out]) = Y W, W(k, o) = Wo[o][k]: dW[i][o] =
   // sum_k Y[i][k] Wo[o][k] on the bf16 matrix cores with Y split into two
@@ -642,14 +693,13 @@ int ispa_drift_prepare(int n_layers, int h, const float* G, float lambda, int64_
       !aligned16(workspace))
     return ISPA_ERR_ALIGN;
   const hipStream_t s = as_stream(stream);
-  RidgeWs w = ridge_layout(workspace, n_layers, h);
-  w.R = linv;  // the forward solve of L Z = I runs in the caller's buffer
+  const RidgeWs w = ridge_layout(workspace, n_layers, h);
   const int nblk = (h + kCholBlock - 1) / kCholBlock;
   const int64_t hh = static_cast<int64_t>(h) * h;
   ISPA_TRY(ispa::launch_copy_add_diag(G, w.L, h, n_layers, lambda, s));
   ISPA_TRY(cholesky(0, nblk, w, h, n_layers, info, s));
   ISPA_TRY(ispa::launch_identity(linv, h, n_layers, s));
-  ISPA_TRY(solve_lower(0, nblk, w, w.R, h, n_layers, s));
+  ISPA_TRY(solve_lower(0, nblk, w, Rhs{linv, h, hh, nullptr}, h, n_layers, s));
   // ||L^{-1}||_F^2 = tr((G + lambda I)^{-1}) -> (h - lambda tr) / n_warm
   ISPA_TRY(ispa::launch_drift_sum(linv, h, h, h, hh, n_layers, w.part, h, lambda,
                                   static_cast<double>(n_warm), nullptr, ref, s));
@@ -666,13 +716,12 @@ int ispa_drift_prepare_factored(int n_layers, int h, float lambda, int64_t n_war
   if (!aligned16(linv) || !aligned16(ref) || !aligned16(workspace)) return ISPA_ERR_ALIGN;
   // the factor and its diagonal-block inverses are where ispa_ridge_solve
   // left them; only the forward solve L Z = I and the trace remain
-  RidgeWs w = ridge_layout(workspace, n_layers, h);
-  w.R = linv;
+  const RidgeWs w = ridge_layout(workspace, n_layers, h);
   const hipStream_t s = as_stream(stream);
   const int nblk = (h + kCholBlock - 1) / kCholBlock;
   const int64_t hh = static_cast<int64_t>(h) * h;
   ISPA_TRY(ispa::launch_identity(linv, h, n_layers, s));
-  ISPA_TRY(solve_lower(0, nblk, w, w.R, h, n_layers, s));
+  ISPA_TRY(solve_lower(0, nblk, w, Rhs{linv, h, hh, nullptr}, h, n_layers, s));
   ISPA_TRY(ispa::launch_drift_sum(linv, h, h, h, hh, n_layers, w.part, h, lambda,
                                   static_cast<double>(n_warm), nullptr, ref, s));
   return ISPA_OK;

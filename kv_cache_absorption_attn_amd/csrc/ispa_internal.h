@@ -109,6 +109,7 @@ struct GemmF32Params {
   float alpha, beta;
   int batch;
   int tri;                   // 0 all tiles; 1 only tiles with tile_m >= tile_n
+  const int* layer_mask;     // optional [batch]: entries with mask 0 are skipped
 };
 hipError_t launch_gemm_f32(const GemmF32Params& p, hipStream_t stream);
 
@@ -121,10 +122,32 @@ struct RidgeResidParams {
   const float* Y;
   float* S;
   double lam;
+  const int* layer_mask;     // optional [batch]: entries with mask 0 are skipped
 };
 hipError_t launch_ridge_resid_f64(const RidgeResidParams& p, hipStream_t stream);
-// y[i] += x[i] over n fp32 elements (n % 4 == 0, 16-byte aligned).
-hipError_t launch_add_inplace(float* y, const float* x, int64_t n, hipStream_t stream);
+// y[b][i] += x[b][i] over batch blocks of n fp32 elements each (n % 4 == 0,
+// 16-byte aligned); blocks whose layer_mask entry is 0 are skipped (no mask:
+// all of them).
+hipError_t launch_add_inplace(float* y, const float* x, int64_t n, int batch,
+                              const int* layer_mask, hipStream_t stream);
+
+// Probe estimate of the refinement's need (see ispa_ridge_solve). For each
+// layer b of an h x h problem with 8 probe columns:
+//   launch_probe_wz:  Q[b] = W[b] Z, W(k, o) = Wo[b][o][k] (bf16, nn.Linear
+//                     layout), Z[o][j] = +-1 from a fixed hash of (o, j);
+//                     Q fp64 [h][8].
+//   launch_mv8_f64:   Y[b] = X[b] Q[b] with X fp32 [h][h] row-major, Q and Y
+//                     fp64 [h][8], accumulated in fp64.
+//   launch_probe_resid: R[b] = A[b] - T[b] - lam B[b], written as fp32 [h][8].
+//   launch_probe_flag: flag[b] = 1 unless ||E[b]||_F <= tol ||B[b]||_F (fp64
+//                     sums in a fixed order; NaN flags 1).
+hipError_t launch_probe_wz(const uint16_t* Wo, double* Q, int h, int batch, hipStream_t stream);
+hipError_t launch_mv8_f64(const float* X, const double* Q, double* Y, int h, int batch,
+                          hipStream_t stream);
+hipError_t launch_probe_resid(const double* A, const double* T, const double* B, double lam,
+                              float* R, int h, int batch, hipStream_t stream);
+hipError_t launch_probe_flag(const float* E, const double* B, double tol, int* flag, int h,
+                             int batch, hipStream_t stream);
 
 // ---------------------------------------------------------------- ridge pieces
 hipError_t launch_copy_add_diag(const float* G, float* L, int h, int batch, float lam,

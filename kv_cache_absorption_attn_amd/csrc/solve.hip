@@ -125,14 +125,145 @@ __global__ __launch_bounds__(256) void potrf_block_kernel(float* __restrict__ L,
 
 // y += x elementwise (float4; the refinement's Y = Y0 + correction).
 __global__ void add_inplace_kernel(float* __restrict__ y, const float* __restrict__ x,
-                                   int64_t n4) {
+                                   int64_t n4, const int* __restrict__ mask) {
+  const int b = blockIdx.y;
+  if (mask && !mask[b]) return;
+  float4* yb = reinterpret_cast<float4*>(y) + b * n4;
+  const float4* xb = reinterpret_cast<const float4*>(x) + b * n4;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n4;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float4 a = reinterpret_cast<float4*>(y)[i];
-    const float4 b = reinterpret_cast<const float4*>(x)[i];
-    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-    reinterpret_cast<float4*>(y)[i] = a;
+    float4 a = yb[i];
+    const float4 c = xb[i];
+    a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+    yb[i] = a;
   }
+}
+
+// ------------------------------------------------------------ refinement probes
+// Eight probe columns z_j (j < 8) with entries +-1: bit j of a hash of the row
+// index (a 32-bit integer mix; any fixed pseudo-random signs serve).
+__device__ __forceinline__ uint32_t probe_bits(uint32_t o) {
+  uint32_t x = o * 0x9E3779B1u + 0x7F4A7C15u;
+  x ^= x >> 16;
+  x *= 0x7FEB352Du;
+  x ^= x >> 15;
+  x *= 0x846CA68Bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// Q[b][k][j] = sum_o Wo[b][o][k] z_j(o): one thread per k, the signs of a
+// 256-row chunk of o staged in LDS.
+__global__ __launch_bounds__(256) void probe_wz_kernel(const uint16_t* __restrict__ Wo,
+                                                       double* __restrict__ Q, int h) {
+  __shared__ uint32_t zs[256];
+  const int b = blockIdx.y;
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  const uint16_t* W = Wo + static_cast<int64_t>(b) * h * h;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int o0 = 0; o0 < h; o0 += 256) {
+    __syncthreads();
+    zs[threadIdx.x] = probe_bits(static_cast<uint32_t>(o0 + threadIdx.x));
+    __syncthreads();
+    const int n = h - o0 < 256 ? h - o0 : 256;
+    if (k < h) {
+      for (int t = 0; t < n; ++t) {
+        const float w = bf16_bits_to_f32(W[static_cast<int64_t>(o0 + t) * h + k]);
+        const uint32_t z = zs[t];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += ((z >> j) & 1u) ? w : -w;
+      }
+    }
+  }
+  if (k < h) {
+    double* q = Q + (static_cast<int64_t>(b) * h + k) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = acc[j];
+  }
+}
+
+// Y[b] = X[b] Q[b] (X fp32 h x h, Q fp64 h x 8), fp64 accumulation. A block of
+// 256 threads owns 64 rows; thread t takes row t % 64 and probes 2 (t / 64)
+// and 2 (t / 64) + 1; 64 x 64 tiles of X and 64 rows of Q go through LDS.
+__global__ __launch_bounds__(256) void mv8_f64_kernel(const float* __restrict__ X,
+                                                      const double* __restrict__ Q,
+                                                      double* __restrict__ Y, int h) {
+  __shared__ float xs[64][65];
+  __shared__ double qs[64][8];
+  const int b = blockIdx.y;
+  const int row0 = blockIdx.x * 64;
+  const int t = threadIdx.x, r = t % 64, p = t / 64;
+  const float* Xb = X + static_cast<int64_t>(b) * h * h;
+  const double* Qb = Q + static_cast<int64_t>(b) * h * 8;
+  double a0 = 0.0, a1 = 0.0;
+  for (int k0 = 0; k0 < h; k0 += 64) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = t + 256 * e, rr = idx / 16, c4 = (idx % 16) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row0 + rr < h && k0 + c4 < h)
+        v = *reinterpret_cast<const float4*>(Xb + static_cast<int64_t>(row0 + rr) * h + k0 + c4);
+      xs[rr][c4] = v.x;
+      xs[rr][c4 + 1] = v.y;
+      xs[rr][c4 + 2] = v.z;
+      xs[rr][c4 + 3] = v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = t + 256 * e, kk = idx / 8, j = idx % 8;
+      qs[kk][j] = k0 + kk < h ? Qb[static_cast<int64_t>(k0 + kk) * 8 + j] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 64; ++kk) {
+      const double x = xs[r][kk];
+      a0 = fma(x, qs[kk][2 * p], a0);
+      a1 = fma(x, qs[kk][2 * p + 1], a1);
+    }
+  }
+  if (row0 + r < h) {
+    double* y = Y + (static_cast<int64_t>(b) * h + row0 + r) * 8 + 2 * p;
+    y[0] = a0;
+    y[1] = a1;
+  }
+}
+
+// R[b] = A[b] - T[b] - lam B[b] (h x 8), rounded to fp32 for the solve.
+__global__ void probe_resid_kernel(const double* __restrict__ A, const double* __restrict__ T,
+                                   const double* __restrict__ B, double lam, float* __restrict__ R,
+                                   int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    R[i] = static_cast<float>(A[i] - T[i] - lam * B[i]);
+}
+
+// flag[b] = !(||E[b]|| <= tol ||B[b]||): one block per layer, fixed-order sums.
+__global__ __launch_bounds__(256) void probe_flag_kernel(const float* __restrict__ E,
+                                                         const double* __restrict__ B, double tol,
+                                                         int* __restrict__ flag, int h) {
+  __shared__ double se[256], sb[256];
+  const int b = blockIdx.x;
+  const int64_t n = static_cast<int64_t>(h) * 8;
+  const float* e = E + b * n;
+  const double* v = B + b * n;
+  double ae = 0.0, ab = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    const double x = e[i];
+    ae = fma(x, x, ae);
+    ab = fma(v[i], v[i], ab);
+  }
+  se[threadIdx.x] = ae;
+  sb[threadIdx.x] = ab;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      se[threadIdx.x] += se[threadIdx.x + s];
+      sb[threadIdx.x] += sb[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) flag[b] = (se[0] <= tol * tol * sb[0]) ? 0 : 1;
 }
 
 // dst[b](j, i) = src[b](i, j) for an h x h matrix, 32 x 32 tiles via LDS.
@@ -379,12 +510,45 @@ hipError_t launch_potrf_block(float* L, float* Linv, int h, int k0, int nb, int 
   return hipGetLastError();
 }
 
-hipError_t launch_add_inplace(float* y, const float* x, int64_t n, hipStream_t stream) {
+hipError_t launch_add_inplace(float* y, const float* x, int64_t n, int batch,
+                              const int* layer_mask, hipStream_t stream) {
   const int64_t n4 = n / 4;
-  if (n4 == 0) return hipSuccess;
+  if (n4 == 0 || batch <= 0) return hipSuccess;
   const int64_t blocks = (n4 + 255) / 256;
-  hipLaunchKernelGGL(add_inplace_kernel, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)),
-                     dim3(256), 0, stream, y, x, n4);
+  hipLaunchKernelGGL(add_inplace_kernel,
+                     dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024), batch), dim3(256),
+                     0, stream, y, x, n4, layer_mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_wz(const uint16_t* Wo, double* Q, int h, int batch, hipStream_t stream) {
+  if (h <= 0 || batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(probe_wz_kernel, dim3((h + 255) / 256, batch), dim3(256), 0, stream, Wo, Q,
+                     h);
+  return hipGetLastError();
+}
+
+hipError_t launch_mv8_f64(const float* X, const double* Q, double* Y, int h, int batch,
+                          hipStream_t stream) {
+  if (h <= 0 || batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mv8_f64_kernel, dim3((h + 63) / 64, batch), dim3(256), 0, stream, X, Q, Y, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_resid(const double* A, const double* T, const double* B, double lam,
+                              float* R, int h, int batch, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(h) * 8 * batch;
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(probe_resid_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                     dim3(256), 0, stream, A, T, B, lam, R, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_flag(const float* E, const double* B, double tol, int* flag, int h,
+                             int batch, hipStream_t stream) {
+  if (h <= 0 || batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(probe_flag_kernel, dim3(batch), dim3(256), 0, stream, E, B, tol, flag, h);
   return hipGetLastError();
 }
 

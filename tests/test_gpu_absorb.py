@@ -245,6 +245,30 @@ def test_rank_deficient_statistics(h, n):
     assert abs(er[0] - er_ref) <= eps_tol(er_ref, h), (er[0], er_ref)
 
 
+def test_refinement_decided_per_layer():
+    """One batched solve over layers that need the refinement step (200
+    tokens at h = 1024: the fp32 solve alone is off by ~3e-3) and a layer that
+    does not (4000 tokens, well conditioned): every layer's dW within 1e-3 of
+    the oracle, so a refinement skipped where it was needed, or applied to the
+    wrong layer, fails."""
+    lam, h = 1e-2, 1024
+    log("per-layer refinement h=1024: rank-deficient, full-rank, rank-deficient")
+    stats = []
+    for l, n in enumerate((200, 4000, 200)):
+        x = wl.random_bf16((n, h), 0.3, 161 + 7 * l)
+        d = wl.random_bf16((n, h), 0.1, 162 + 7 * l)
+        stats.append(tuple(a.astype(np.float32).astype(np.float64)
+                           for a in orc.gram_statistics([x], [d])))
+    wo = np.stack([wl.random_bf16((h, h), 1.0 / np.sqrt(h), 163 + 7 * l) for l in range(3)])
+    G, C, _ = f32_dev(*(np.stack([st[i] for st in stats]) for i in range(3)))
+    dW, info, _ = ridge_gpu(G, C, dev_bf16(wo), lam)
+    assert np.all(info.cpu().numpy() == 0)
+    for l, (g, c, _) in enumerate(stats):
+        err = relfro(host(dW[l]), orc.ridge_delta_w(g, c, wo[l], lam))
+        log(f"  layer {l}: dW rel fro {err:.2e}")
+        assert err <= DW_REL
+
+
 # ------------------------------------------------------------------ ridge + score
 
 def _synthetic_stats(L, h, n, seed):
