@@ -18,7 +18,6 @@ namespace ispa {
 namespace {
 
 constexpr int kNB = 128;
-constexpr int kLdsLd = kNB + 1;
 
 __global__ void copy_add_diag_kernel(const float* __restrict__ G, float* __restrict__ L, int h,
                                      float lam) {
@@ -44,80 +43,164 @@ __global__ void copy_add_diag_kernel(const float* __restrict__ G, float* __restr
 // non-positive pivot (0 when the block, and all earlier ones, were fine); a
 // failing pivot is replaced by 1 so the factorisation still runs to the end
 // with finite values.
+//
+// Register-blocked: thread t holds the 8 x 8 block (t / 16, t % 16) of the
+// block's lower triangle, first of the factor, then of its inverse (blocks
+// above the diagonal stay zero). Each step broadcasts one column of the
+// factor (and, for the inverse, one row) through LDS and every thread
+// updates its own block in registers: two barriers per column, instead of a
+// chain of dependent LDS read-modify-writes per element and column.
 __global__ __launch_bounds__(256) void potrf_block_kernel(float* __restrict__ L,
                                                           float* __restrict__ Linv, int h,
                                                           int k0, int nb, int* __restrict__ info,
                                                           int info_first) {
-  extern __shared__ float lds[];
-  float* A = lds;                   // [kNB][kLdsLd]
-  float* X = lds + kNB * kLdsLd;    // [kNB][kLdsLd]
-  __shared__ float s_inv;
+  __shared__ float s_col[kNB];  // a column of the factor below the diagonal
+  __shared__ float s_row[kNB];  // a row of the inverse
+  __shared__ float s_dg[kNB];   // the diagonal of the factor
   __shared__ int s_fail;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int64_t hh = static_cast<int64_t>(h) * h;
-  float* Lb = L + b * hh;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int bi = t / 16, bj = t % 16;
+  const int i0 = 8 * bi, c0 = 8 * bj;
+  const bool lower = bi >= bj;
+  float* Lb = L + b * static_cast<int64_t>(h) * h + static_cast<int64_t>(k0) * h + k0;
 
-  for (int e = tid; e < nb * nb; e += blockDim.x) {
-    const int i = e / nb, j = e % nb;
-    A[i * kLdsLd + j] = (j <= i) ? Lb[static_cast<int64_t>(k0 + i) * h + k0 + j] : 0.f;
+  float a[8][8];
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) a[ii][cc] = 0.f;
+  if (lower && c0 < nb) {
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const int i = i0 + ii;
+      if (i >= nb) continue;
+      const float4 lo = *reinterpret_cast<const float4*>(Lb + static_cast<int64_t>(i) * h + c0);
+      const float4 hi = *reinterpret_cast<const float4*>(Lb + static_cast<int64_t>(i) * h + c0 + 4);
+      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) a[ii][cc] = (c0 + cc <= i) ? v[cc] : 0.f;
+    }
   }
-  if (tid == 0) s_fail = 0;
+  if (t == 0) s_fail = 0;
   __syncthreads();
 
-  const int ti = tid / 16, tc = tid % 16;
-  for (int j = 0; j < nb; ++j) {
-    if (tid == 0) {
-      float d = A[j * kLdsLd + j];
-      if (!(d > 0.f)) {
-        if (s_fail == 0) s_fail = j + 1;
-        d = 1.f;
+  // right-looking factorisation, one column j at a time
+  for (int jb = 0; jb < kNB / 8; ++jb) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = 8 * jb + jj;
+      if (j >= nb) continue;  // uniform
+      if (bi == jb && bj == jb) {
+        float d = a[jj][jj];
+        if (!(d > 0.f)) {
+          if (s_fail == 0) s_fail = j + 1;
+          d = 1.f;
+        }
+        const float r = sqrtf(d);
+        a[jj][jj] = r;
+        s_dg[j] = r;
       }
-      const float r = sqrtf(d);
-      A[j * kLdsLd + j] = r;
-      s_inv = 1.f / r;
-    }
-    __syncthreads();
-    const float inv = s_inv;
-    for (int i = j + 1 + tid; i < nb; i += blockDim.x) A[i * kLdsLd + j] *= inv;
-    __syncthreads();
-    // trailing update of the lower triangle: A[i][c] -= A[i][j] A[c][j], j < c <= i
-    const int first = j + 1;
-    for (int i = first + ((ti - first) % 16 + 16) % 16; i < nb; i += 16) {
-      const float aij = A[i * kLdsLd + j];
-      for (int c = first + ((tc - first) % 16 + 16) % 16; c <= i; c += 16) {
-        A[i * kLdsLd + c] -= aij * A[c * kLdsLd + j];
+      __syncthreads();
+      if (bj == jb && bi >= jb) {
+        const float inv = 1.f / s_dg[j];
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int i = i0 + ii;
+          if (i > j && i < nb) {
+            a[ii][jj] *= inv;
+            s_col[i] = a[ii][jj];
+          }
+        }
+      }
+      __syncthreads();
+      // A(i, c) -= L(i, j) L(c, j) for j < c <= i
+      if (lower && i0 + 7 > j) {
+        float li[8], lc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          li[e] = s_col[i0 + e];
+          lc[e] = s_col[c0 + e];
+        }
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const int i = i0 + ii, c = c0 + cc;
+            if (c > j && c <= i && i < nb) a[ii][cc] = fmaf(-li[ii], lc[cc], a[ii][cc]);
+          }
       }
     }
-    __syncthreads();
   }
 
-  // inverse of the lower-triangular factor, one column per thread
-  if (tid < nb) {
-    const int c = tid;
-    for (int i = 0; i < nb; ++i) {
-      float v;
-      if (i < c) {
-        v = 0.f;
-      } else if (i == c) {
-        v = 1.f / A[c * kLdsLd + c];
-      } else {
-        float s = 0.f;
-        for (int k = c; k < i; ++k) s = fmaf(A[i * kLdsLd + k], X[k * kLdsLd + c], s);
-        v = -s / A[i * kLdsLd + i];
+  // inverse X = L^-1 by rows: X(k, c) = (delta_kc - sum_{m<k} L(k, m) X(m, c)) / L(k, k),
+  // the sums kept per element and updated once row k is final
+  float x[8][8];
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) x[ii][cc] = (i0 + ii == c0 + cc && i0 + ii < nb) ? 1.f : 0.f;
+  for (int kb = 0; kb < kNB / 8; ++kb) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int k = 8 * kb + kk;
+      if (k >= nb) continue;  // uniform
+      if (bi == kb && bj <= kb) {
+        const float dinv = 1.f / s_dg[k];
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const int c = c0 + cc;
+          if (c <= k) {
+            x[kk][cc] *= dinv;
+            s_row[c] = x[kk][cc];
+          }
+        }
       }
-      X[i * kLdsLd + c] = v;
+      if (bj == kb && bi >= kb) {
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int i = i0 + ii;
+          if (i > k && i < nb) s_col[i] = a[ii][kk];
+        }
+      }
+      __syncthreads();
+      // X(i, c) -= L(i, k) X(k, c) for i > k, c <= k
+      if (lower && i0 + 7 > k && c0 <= k) {
+        float li[8], xr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          li[e] = s_col[i0 + e];
+          xr[e] = s_row[c0 + e];
+        }
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii)
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const int i = i0 + ii, c = c0 + cc;
+            if (i > k && i < nb && c <= k) x[ii][cc] = fmaf(-li[ii], xr[cc], x[ii][cc]);
+          }
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
 
   float* Lib = Linv + b * static_cast<int64_t>(h) * kNB + static_cast<int64_t>(k0) * kNB;
-  for (int e = tid; e < nb * nb; e += blockDim.x) {
-    const int i = e / nb, j = e % nb;
-    if (j <= i) Lb[static_cast<int64_t>(k0 + i) * h + k0 + j] = A[i * kLdsLd + j];
-    Lib[i * kNB + j] = X[i * kLdsLd + j];
+  if (c0 < nb) {
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const int i = i0 + ii;
+      if (i >= nb) continue;
+      if (lower) {
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+          if (c0 + cc <= i) Lb[static_cast<int64_t>(i) * h + c0 + cc] = a[ii][cc];
+      }
+      *reinterpret_cast<float4*>(Lib + i * kNB + c0) =
+          make_float4(x[ii][0], x[ii][1], x[ii][2], x[ii][3]);
+      *reinterpret_cast<float4*>(Lib + i * kNB + c0 + 4) =
+          make_float4(x[ii][4], x[ii][5], x[ii][6], x[ii][7]);
+    }
   }
-  if (tid == 0) {
+  if (t == 0) {
     if (info_first) info[b] = s_fail ? k0 + s_fail : 0;
     else if (s_fail && info[b] == 0) info[b] = k0 + s_fail;
   }
@@ -499,13 +582,7 @@ hipError_t launch_copy_add_diag(const float* G, float* L, int h, int batch, floa
 
 hipError_t launch_potrf_block(float* L, float* Linv, int h, int k0, int nb, int batch, int* info,
                               int info_first, hipStream_t stream) {
-  const size_t lds = 2 * kNB * kLdsLd * sizeof(float);
-  // set on every call (cheap): no process-wide state, valid for any device
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(potrf_block_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(potrf_block_kernel, dim3(batch), dim3(256), lds, stream, L, Linv, h, k0, nb,
+  hipLaunchKernelGGL(potrf_block_kernel, dim3(batch), dim3(256), 0, stream, L, Linv, h, k0, nb,
                      info, info_first);
   return hipGetLastError();
 }
