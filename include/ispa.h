@@ -491,8 +491,9 @@ typedef struct ispa_kv_view {
   /* The three KV segments ispa_attn_decomp takes, in its order. When
    * split_ok != 0 they are exactly (sink, current, history); otherwise (an
    * F-layer whose ring has wrapped) their union is sink + history + current
-   * and only the full outputs are meaningful. A segment of length 0 has
-   * NULL pointers. */
+   * and only the full outputs of ispa_attn_decomp over them are meaningful
+   * (ispa_kv_attn forms the split outputs in that case too). A segment of
+   * length 0 has NULL pointers. */
   const void* seg_k[3];
   const void* seg_v[3];
   int64_t seg_n[3];
@@ -566,11 +567,11 @@ int64_t ispa_kv_resident_bytes(const ispa_kv_cache* cache);
 
 /*
  * ispa_attn_decomp of one layer over its cache for the current chunk:
- * q [n_q, n_heads, head_dim] bf16, outputs as there. The split outputs
- * (o_local, lse_local, o_hist, lse_hist, d_out) need split_ok (see
- * ispa_kv_view); otherwise ISPA_ERR_UNSUPPORTED. For an L-layer the history
- * is empty. Other errors as for ispa_attn_decomp, plus ISPA_ERR_SHAPE for
- * the layer index.
+ * q [n_q, n_heads, head_dim] bf16, outputs as there. For an F-layer whose
+ * ring has wrapped (split_ok == 0) the split outputs are formed over its
+ * history in the ring's two pieces (slots after the current one, then the
+ * slots before it). For an L-layer the history is empty. Errors as for
+ * ispa_attn_decomp, plus ISPA_ERR_SHAPE for the layer index.
  */
 int ispa_kv_attn(const ispa_kv_cache* cache, int layer, const void* q,
                  int64_t n_q, float sm_scale, void* o_local, float* lse_local,
@@ -613,9 +614,9 @@ int ispa_kv_layer_forward(const ispa_kv_cache* cache, int layer, const void* q,
  *    stride drift_stride). If one exceeds drift_threshold (or is NaN),
  *    end_chunk restores the L-layers (original W, history restarting with
  *    the next chunk) and enters warmup again: event RECALIBRATE.
- * The split attention of a warmup needs every F-layer's history in one
- * piece, i.e. a ring that has not wrapped (ISPA_ERR_UNSUPPORTED otherwise):
- * give hist_capacity at least the stream's length when recalibration is on.
+ * A warmup after a recalibration attends each F-layer's history as the
+ * cache holds it: the hist_capacity most recent tokens, also once the ring
+ * has wrapped.
  *
  * Memory: wo [n_layers][h, h] bf16 (original weights, read, kept unchanged
  * by the caller), w_active [n_layers][h, h] bf16 (written: the weights in

@@ -273,20 +273,23 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
   const int nt0 = static_cast<int>((p.n[0] + kKTile - 1) / kKTile);
   const int nt1 = static_cast<int>((p.n[1] + kKTile - 1) / kKTile);
   const int nt2 = static_cast<int>((p.n[2] + kKTile - 1) / kKTile);
+  const int nt3 = static_cast<int>((p.n[3] + kKTile - 1) / kKTile);
   const int n_local_tiles = nt0 + nt1;
   const bool split = p.mode == 0;
   const bool run_hist = !(split && !p.need_hist);
-  const int T = n_local_tiles + (run_hist ? nt2 : 0);
+  const int T = n_local_tiles + (run_hist ? nt2 + nt3 : 0);
+  const bool has_hist = p.n[2] + p.n[3] > 0;
 
   auto tile_of = [&](int idx, Seg& sg, int64_t& row0, int& valid) {
-    const bool s0 = idx < nt0, s1 = !s0 && idx < n_local_tiles;
-    const int t = s0 ? idx : (s1 ? idx - nt0 : idx - n_local_tiles);
-    sg.k = s0 ? p.k[0] : (s1 ? p.k[1] : p.k[2]);
-    sg.v = s0 ? p.v[0] : (s1 ? p.v[1] : p.v[2]);
-    sg.n = s0 ? p.n[0] : (s1 ? p.n[1] : p.n[2]);
+    const int h0 = n_local_tiles + nt2;  // first tile of the second history piece
+    const int g = idx < nt0 ? 0 : (idx < n_local_tiles ? 1 : (idx < h0 ? 2 : 3));
+    const int t = idx - (g == 0 ? 0 : (g == 1 ? nt0 : (g == 2 ? n_local_tiles : h0)));
+    sg.k = p.k[g];
+    sg.v = p.v[g];
+    sg.n = p.n[g];
     if constexpr (F8) {
-      sg.k = reinterpret_cast<const uint16_t*>(s0 ? p.k8[0] : (s1 ? p.k8[1] : p.k8[2]));
-      sg.ksc = s0 ? p.ksc[0] : (s1 ? p.ksc[1] : p.ksc[2]);
+      sg.k = reinterpret_cast<const uint16_t*>(p.k8[g]);
+      sg.ksc = p.ksc[g];
     }
     row0 = static_cast<int64_t>(t) * kKTile;
     const int64_t rem = sg.n - row0;
@@ -579,12 +582,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int work) 
             inv = 1.f / lt;
             lse_f2 = m_run[qb] + __builtin_amdgcn_logf(lt);
           } else {
-            if (p.n[2] > 0) {
+            if (has_hist) {
               inv = 1.f / lt;
               lse2 = m_run[qb] + __builtin_amdgcn_logf(lt);
             }
             lse_f2 = lse_loc2[qb];
-            if (p.n[2] > 0) {
+            if (has_hist) {
               const float mm = fmaxf(lse_loc2[qb], lse2);
               lse_f2 = mm + __builtin_amdgcn_logf(__builtin_amdgcn_exp2f(lse_loc2[qb] - mm) +
                                                   __builtin_amdgcn_exp2f(lse2 - mm));

@@ -226,21 +226,24 @@ int attn_setup(const void* q, int64_t n_q, const void* k_sink, const void* v_sin
                int head_dim, float sm_scale, void* o_local, float* lse_local, void* o_hist,
                float* lse_hist, void* o_full, float* lse_full, void* d_out,
                ispa::AttnParams* out, bool* run, void* xt = nullptr, void* dt = nullptr,
-               int64_t ldt = 0) {
+               int64_t ldt = 0, const void* k_hist2 = nullptr, const void* v_hist2 = nullptr,
+               int64_t n_hist2 = 0) {
   *run = false;
-  if (n_q < 0 || n_sink < 0 || n_cur < 0 || n_hist < 0 || n_heads < 1) return ISPA_ERR_SHAPE;
+  if (n_q < 0 || n_sink < 0 || n_cur < 0 || n_hist < 0 || n_hist2 < 0 || n_heads < 1)
+    return ISPA_ERR_SHAPE;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return ISPA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return ISPA_ERR_UNSUPPORTED;
   if (!q && n_q > 0) return ISPA_ERR_NULL;
   if ((n_sink > 0 && (!k_sink || !v_sink)) || (n_cur > 0 && (!k_cur || !v_cur)) ||
-      (n_hist > 0 && (!k_hist || !v_hist)))
+      (n_hist > 0 && (!k_hist || !v_hist)) || (n_hist2 > 0 && (!k_hist2 || !v_hist2)))
     return ISPA_ERR_NULL;
   if (!o_local && !lse_local && !o_hist && !lse_hist && !o_full && !lse_full && !d_out && !xt &&
       !dt)
     return ISPA_ERR_NULL;
   if (n_sink + n_cur < 1) return ISPA_ERR_SHAPE;
-  const void* ptrs[] = {q, k_sink, v_sink, k_cur, v_cur, k_hist, v_hist, o_local, lse_local,
-                        o_hist, lse_hist, o_full, lse_full, d_out, xt, dt};
+  const void* ptrs[] = {q,         k_sink,   v_sink, k_cur,  v_cur,    k_hist,
+                        v_hist,    k_hist2,  v_hist2, o_local, lse_local, o_hist,
+                        lse_hist,  o_full,   lse_full, d_out,  xt,       dt};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return ISPA_ERR_ALIGN;
   const int64_t qtiles = (n_q + ispa::attn_q_tile_min() - 1) / ispa::attn_q_tile_min();
@@ -258,6 +261,9 @@ int attn_setup(const void* q, int64_t n_q, const void* k_sink, const void* v_sin
   p.k[2] = static_cast<const uint16_t*>(k_hist);
   p.v[2] = static_cast<const uint16_t*>(v_hist);
   p.n[2] = n_hist;
+  p.k[3] = static_cast<const uint16_t*>(k_hist2);
+  p.v[3] = static_cast<const uint16_t*>(v_hist2);
+  p.n[3] = n_hist2;
   p.n_q = n_q;
   p.n_heads = n_heads;
   p.scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
@@ -278,6 +284,32 @@ int attn_setup(const void* q, int64_t n_q, const void* k_sink, const void* v_sin
   *run = true;
   return ISPA_OK;
 }
+
+}  // namespace
+
+namespace ispa {
+
+int attn_decomp_two_piece_history(const void* q, int64_t n_q, const void* k_sink,
+                                  const void* v_sink, int64_t n_sink, const void* k_cur,
+                                  const void* v_cur, int64_t n_cur, const void* k_hist,
+                                  const void* v_hist, int64_t n_hist, const void* k_hist2,
+                                  const void* v_hist2, int64_t n_hist2, int n_heads, int head_dim,
+                                  float sm_scale, void* o_local, float* lse_local, void* o_hist,
+                                  float* lse_hist, void* o_full, float* lse_full, void* d_out,
+                                  void* stream) {
+  AttnParams p{};
+  bool run = false;
+  const int st = attn_setup(q, n_q, k_sink, v_sink, n_sink, k_cur, v_cur, n_cur, k_hist, v_hist,
+                            n_hist, n_heads, head_dim, sm_scale, o_local, lse_local, o_hist,
+                            lse_hist, o_full, lse_full, d_out, &p, &run, nullptr, nullptr, 0,
+                            k_hist2, v_hist2, n_hist2);
+  if (st != ISPA_OK || !run) return st;
+  return hip_status(launch_attn_decomp(p, head_dim, as_stream(stream)));
+}
+
+}  // namespace ispa
+
+namespace {
 
 // Workspace of the E4M3 attention: query codes, scales and shifts, then per
 // segment the key codes and tile scales.

@@ -9,9 +9,12 @@ namespace ispa {
 // ---------------------------------------------------------------- attention
 struct AttnParams {
   const uint16_t* q;         // [n_q, n_heads, D] bf16
-  const uint16_t* k[3];      // segments: 0 sink, 1 current, 2 history
-  const uint16_t* v[3];
-  int64_t n[3];
+  // segments: 0 sink and 1 current (the local set), 2 and 3 history (one
+  // piece, or the two pieces of a ring buffer that has wrapped; n[3] = 0
+  // otherwise)
+  const uint16_t* k[4];
+  const uint16_t* v[4];
+  int64_t n[4];
   int64_t n_q;
   int n_heads;
   float scale_log2;          // softmax scale * log2(e)
@@ -38,8 +41,8 @@ struct AttnParams {
   // qmu [n_heads, n_q]: scale * q . mu added to every LSE output (or null)
   const uint8_t* q8;
   const float* qsc;
-  const uint8_t* k8[3];
-  const float* ksc[3];
+  const uint8_t* k8[4];
+  const float* ksc[4];
   const float* qmu;
 };
 // Fills p.n_qtiles, then launches.
@@ -53,6 +56,18 @@ struct AttnGroup {
   int n;
 };
 hipError_t launch_attn_grouped(AttnGroup grp, int head_dim, hipStream_t stream);
+
+// ispa_attn_decomp with the history in two pieces (hist, then hist2: the two
+// ranges of a ring buffer that has wrapped): the same arguments, checks,
+// outputs and errors; the second piece may be empty.
+int attn_decomp_two_piece_history(const void* q, int64_t n_q, const void* k_sink,
+                                  const void* v_sink, int64_t n_sink, const void* k_cur,
+                                  const void* v_cur, int64_t n_cur, const void* k_hist,
+                                  const void* v_hist, int64_t n_hist, const void* k_hist2,
+                                  const void* v_hist2, int64_t n_hist2, int n_heads, int head_dim,
+                                  float sm_scale, void* o_local, float* lse_local, void* o_hist,
+                                  float* lse_hist, void* o_full, float* lse_full, void* d_out,
+                                  void* stream);
 
 // E4M3 attention operands (head_dim 128).
 struct KeySegs {

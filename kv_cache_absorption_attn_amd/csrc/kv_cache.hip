@@ -29,6 +29,7 @@
 #include <vector>
 
 #include "ispa.h"
+#include "ispa_internal.h"
 
 namespace {
 
@@ -392,7 +393,20 @@ int ispa_kv_attn(const ispa_kv_cache* cache, int layer, const void* q, int64_t n
   ispa_kv_view v;
   fill_view(cache, layer, &v);
   const bool split = o_local || lse_local || o_hist || lse_hist || d_out;
-  if (split && !v.split_ok) return ISPA_ERR_UNSUPPORTED;
+  if (split && !v.split_ok) {
+    // a wrapped ring: sink | slots [0, s) | current (slot s) | slots (s, S);
+    // the history is slots (s, S) then slots [0, s), two pieces
+    const LayerKV& L = cache->layers[layer];
+    const int64_t s = L.chunk % cache->n_slots;
+    char* kb = L.k.base;
+    char* vb = L.v.base;
+    const int64_t first = cache->rows_bytes(cache->n_sink);
+    return ispa::attn_decomp_two_piece_history(
+        q, n_q, v.k_sink, v.v_sink, cache->n_sink, v.k_cur, v.v_cur, cache->n_cur, v.seg_k[2],
+        v.seg_v[2], v.seg_n[2], kb + first, vb + first, s * cache->n_cur, cache->n_heads,
+        cache->head_dim, sm_scale, o_local, lse_local, o_hist, lse_hist, o_full, lse_full, d_out,
+        stream);
+  }
   return ispa_attn_decomp(q, n_q, v.seg_k[0], v.seg_v[0], v.seg_n[0], v.seg_k[1], v.seg_v[1],
                           v.seg_n[1], v.seg_k[2], v.seg_v[2], v.seg_n[2], cache->n_heads,
                           cache->head_dim, sm_scale, o_local, lse_local, o_hist, lse_hist, o_full,

@@ -90,8 +90,9 @@ class OracleSession:
     """The oracle's replay of the session: the same life cycle, decided on
     the oracle's own numbers."""
 
-    def __init__(self, wo, n_sink, scale, lam, k_select, t_warm, tau, quant=False):
+    def __init__(self, wo, n_sink, scale, lam, k_select, t_warm, tau, quant=False, cap=None):
         self.quant = quant                   # W8A8 projections, E4M3 attention when streaming
+        self.cap = cap                       # history capacity in chunks (None: unbounded)
         self.mu = {}
         self.wo = [np.asarray(w, dtype=np.float64) for w in wo]
         self.L = len(wo)
@@ -131,7 +132,7 @@ class OracleSession:
             g, n_warm = self.stats[l]
             self.drift[l] = orc.drift_score(x, g, self.lam, n_warm)
             return o, self.proj(o, l)
-        hist = list(range(self.first[l], c))
+        hist = [i for i in range(self.first[l], c) if self.cap is None or i >= c - self.cap]
         kh = np.concatenate([kc[i] for i in hist]) if hist else empty
         vh = np.concatenate([vc[i] for i in hist]) if hist else empty
         if streaming_fp8:
@@ -203,7 +204,16 @@ def test_session_quantized_life_cycle():
     life_cycle(nh=1, d=128, flags=ispa.SESSION_W8A8 | ispa.SESSION_FP8_ATTN, y_tol=3e-2)
 
 
-def life_cycle(nh, d, flags, y_tol):
+def test_session_recalibrates_after_ring_wrap():
+    """The life cycle with a history capacity of 3 chunks: the F-layers'
+    rings have wrapped by the time the drift event re-enters the warmup, so
+    the warmup's split attention runs over a history in two pieces (chunks
+    5 and 6: slots after the current one, then before it), against the
+    oracle's replay over the 3 most recent chunks."""
+    life_cycle(nh=2, d=64, flags=0, y_tol=O_RELFRO, cap_chunks=3)
+
+
+def life_cycle(nh, d, flags, y_tol, cap_chunks=16):
     L, ns, nc = 3, 64, 256
     h = nh * d
     scale, lam, K, t_warm, tau = 1.0 / np.sqrt(d), 1e-2, 1, 2, 4.0
@@ -219,9 +229,10 @@ def life_cycle(nh, d, flags, y_tol):
     kc = [[] for _ in range(L)]
     vc = [[] for _ in range(L)]
     sess = ispa.Session(dev_bf16(np.stack(wo)), n_heads=nh, head_dim=d, n_sink=ns, n_cur=nc,
-                        hist_capacity=16 * nc, k_select=K, t_warm=t_warm, sm_scale=scale,
+                        hist_capacity=cap_chunks * nc, k_select=K, t_warm=t_warm, sm_scale=scale,
                         lam=lam, drift_threshold=tau, drift_stride=1, flags=flags)
-    ref = OracleSession(wo, ns, scale, lam, K, t_warm, tau, quant=flags != 0)
+    ref = OracleSession(wo, ns, scale, lam, K, t_warm, tau, quant=flags != 0,
+                        cap=cap_chunks if cap_chunks < n_chunks else None)
     try:
         for l in range(L):
             sess.cache.write(l, dev_bf16(ks[l]), dev_bf16(vs[l]), sink=True)

@@ -101,7 +101,9 @@ def run_split(cache, s, l, c):
 def test_ring_of_full_layers(d):
     """Two F-layers, a history capacity of 3 chunks and 7 chunks: the ring
     fills, wraps, and keeps the 3 most recent chunks. Segment lengths end
-    mid-tile (sink 40, chunk 100 keys; 150 queries)."""
+    mid-tile (sink 40, chunk 100 keys; 150 queries). The split outputs match
+    the oracle at every ring state, also when the wrapped history is in two
+    pieces (the view's three segments then cover it only for full outputs)."""
     L, nh, ns, nc, nq, cap_chunks = 2, 2, 40, 100, 150, 3
     s = Stream(L, nh, d, ns, nc, nq, seed=d)
     cache = ispa.KVCache(L, nh, d, ns, nc, cap_chunks * nc)
@@ -122,11 +124,7 @@ def test_ring_of_full_layers(d):
                 o, y = run_layer(cache, s, l, c, wo[l])
                 o_ref, y_ref = s.oracle(l, c, False, cap_chunks)
                 check_forward(o, y, o_ref, y_ref, f"layer {l} chunk {c}")
-                if v.split_ok:
-                    compare_attention(run_split(cache, s, l, c), s.oracle_split(l, c, cap_chunks))
-                else:
-                    with pytest.raises(ispa.IspaError):
-                        run_split(cache, s, l, c)
+                compare_attention(run_split(cache, s, l, c), s.oracle_split(l, c, cap_chunks))
             resident.append(cache.resident_bytes())
             cache.advance()
         row = nh * d * 2
@@ -187,7 +185,7 @@ def test_wan_shaped_chunks_with_wrap():
     """Frame-sized segments (sink 1560 keys, chunk 4680 keys = 3 frames) with
     a 2-chunk history ring over 5 chunks, 8 heads, 256 queries: the attention
     over the cache at the real segment lengths, including the wrapped ring's
-    out-of-order slots."""
+    out-of-order slots, for the full and the split outputs."""
     L, nh, d, ns, nc, nq, cap = 1, 8, 128, 1560, 4680, 256, 2
     s = Stream(L, nh, d, ns, nc, nq, seed=11)
     cache = ispa.KVCache(L, nh, d, ns, nc, cap * nc)
@@ -201,6 +199,8 @@ def test_wan_shaped_chunks_with_wrap():
             o, y = run_layer(cache, s, 0, c, wo)
             o_ref, y_ref = s.oracle(0, c, False, cap)
             check_forward(o, y, o_ref, y_ref, f"chunk {c}")
+            # split outputs too (chunk 4: the history is slot 2, then slot 0)
+            compare_attention(run_split(cache, s, 0, c), s.oracle_split(0, c, cap))
             cache.advance()
     finally:
         cache.close()
