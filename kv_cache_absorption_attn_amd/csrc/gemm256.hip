@@ -78,16 +78,21 @@ namespace {
 
 enum { kOutBf16 = 0, kOutF32 = 1, kAccF32 = 2 };
 
-template <int OUT, int KB>
+template <int OUT, int KB, int BM>
 __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const int tn) {
   static_assert(KB == 32 || KB == 64, "stages of 32 or 64 k");
-  constexpr int NS = KB == 32 ? 4 : 2;   // ring slots (128 KB of LDS either way)
+  static_assert(BM == 256 || BM == 192, "row tiles of 256 or 192");
+  constexpr int NS = KB == 32 ? 4 : 2;   // ring slots (128 KB of LDS either way at BM 256)
   constexpr int CPR = KB / 8;            // 16-byte chunks of an LDS row
   constexpr int RPI = 64 / CPR;          // rows one load instruction fills
-  constexpr int LPW = 32 / RPI;          // load instructions a wave issues per operand
-  constexpr int LS = 2 * LPW;            // ... per stage
+  constexpr int RWA = BM / 8;            // A rows a wave loads per stage
+  constexpr int LPWA = RWA / RPI;        // load instructions a wave issues for A
+  constexpr int LPWB = 32 / RPI;         // ... for B
+  constexpr int LS = LPWA + LPWB;        // ... per stage
   constexpr int KS = KB / 16;            // MFMA k-steps of a stage
-  __shared__ __attribute__((aligned(16))) uint16_t sa[NS][kBM * KB];
+  constexpr int MI = BM / 64;            // 32-row MFMA blocks of a wave (its rows: BM / 2)
+  static_assert(RWA % RPI == 0, "whole load instructions per wave");
+  __shared__ __attribute__((aligned(16))) uint16_t sa[NS][BM * KB];
   __shared__ __attribute__((aligned(16))) uint16_t sb[NS][kBN * KB];
   // chunk c of row r sits at position c ^ swz(r): the 16 rows of a
   // quarter-wave's fragment reads then cover the 64 banks once
@@ -98,7 +103,7 @@ __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, l32 = lane % 32, hf = lane / 32;
   const int wm = wave / 4, wn = wave % 4;
-  const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
   const int n0 = tn * kBN;
 
   const int nk = (p.k + KB - 1) / KB;
@@ -108,18 +113,24 @@ __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const
   const u32x4 ra2 = desc_of(p.a2 ? p.a2 : p.a);
   const u32x4 rb = desc_of(p.b);
 
-  // wave w loads A rows [32 w, 32 w + 32) and B rows [32 w, 32 w + 32) of a
-  // stage, LPW instructions each; lane -> (row lane / CPR, position lane % CPR)
-  uint32_t va[LPW], vb[LPW];
-  int lrow[LPW];
+  // wave w loads A rows [RWA w, RWA w + RWA) and B rows [32 w, 32 w + 32) of
+  // a stage, LPWA and LPWB instructions; lane -> (row lane / CPR, position
+  // lane % CPR)
+  uint32_t va[LPWA], vb[LPWB];
+  int lrowa[LPWA], lrowb[LPWB];
   const int pc = lane % CPR;
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int row = wave * 32 + RPI * j + lane / CPR;
-    lrow[j] = row;
+  for (int j = 0; j < LPWA; ++j) {
+    const int row = wave * RWA + RPI * j + lane / CPR;
+    lrowa[j] = row;
     int64_t gr = m0 + row;
     if (gr > p.m - 1) gr = p.m - 1;
     va[j] = static_cast<uint32_t>(gr * p.lda * 2 + 16 * pos_of(row, pc));
+  }
+#pragma unroll
+  for (int j = 0; j < LPWB; ++j) {
+    const int row = wave * 32 + RPI * j + lane / CPR;
+    lrowb[j] = row;
     int gb = n0 + row;
     if (gb > p.n - 1) gb = p.n - 1;
     vb[j] = static_cast<uint32_t>(static_cast<int64_t>(gb) * p.ldb * 2 + 16 * pos_of(row, pc));
@@ -133,32 +144,33 @@ __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const
     if (k0 > k_last_chunk) k0 = k_last_chunk;
     return v - 16 * c + 2 * k0;   // same row, chunk at k0 (stage offset not added)
   };
-  // load j (0 .. LS - 1) of stage s into slot (da, db): j < LPW A, else B
+  // load j (0 .. LS - 1) of stage s into slot (da, db): j < LPWA A, else B
   auto dma = [&](int s, uint16_t* da, uint16_t* db, int j) __attribute__((always_inline)) {
     const int kst = s >= nk ? s - nk : s;
     const bool t = tail && kst == nk - 1;
-    const int jj = j % LPW;
-    const int row0 = wave * 32 + RPI * jj;
-    if (j < LPW) {
+    if (j < LPWA) {
+      const int row0 = wave * RWA + RPI * j;
       const u32x4 r = s >= nk ? ra2 : ra1;
-      dma16_asm(r, da + row0 * KB, t ? tail_off(va[jj], lrow[jj], kst) : va[jj],
+      dma16_asm(r, da + row0 * KB, t ? tail_off(va[j], lrowa[j], kst) : va[j],
                 t ? 0 : kst * 2 * KB);
     } else {
-      dma16_asm(rb, db + row0 * KB, t ? tail_off(vb[jj], lrow[jj], kst) : vb[jj],
+      const int jj = j - LPWA;
+      const int row0 = wave * 32 + RPI * jj;
+      dma16_asm(rb, db + row0 * KB, t ? tail_off(vb[jj], lrowb[jj], kst) : vb[jj],
                 t ? 0 : kst * 2 * KB);
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  int ar[4], br[2], apos[4][KS], bpos[2][KS];
+  int ar[MI], br[2], apos[MI][KS], bpos[2][KS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ar[i] = wm * 128 + i * 32 + l32;
+  for (int i = 0; i < MI; ++i) {
+    ar[i] = wm * (BM / 2) + i * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) apos[i][kk] = pos_of(ar[i], 2 * kk + hf);
   }
@@ -202,18 +214,18 @@ __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const
     // the slot freed by the previous stage spread between the first ones
 #pragma unroll
     for (int h2 = 0; h2 < KS / 2; ++h2) {
-      bf16x8 av[2][4], bv[2][2];
+      bf16x8 av[2][MI], bv[2][2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int kk = 2 * h2 + q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[q][i] = frag_at(ca, ar[i], apos[i][kk]);
+        for (int i = 0; i < MI; ++i) av[q][i] = frag_at(ca, ar[i], apos[i][kk]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) bv[q][j] = frag_at(cb, br[j], bpos[j][kk]);
         if (mask) {
           const int k0 = kst * KB + 16 * kk + 8 * hf;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) av[q][i] = mask_k(av[q][i], k0, p.k);
+          for (int i = 0; i < MI; ++i) av[q][i] = mask_k(av[q][i], k0, p.k);
 #pragma unroll
           for (int j = 0; j < 2; ++j) bv[q][j] = mask_k(bv[q][j], k0, p.k);
         }
@@ -221,11 +233,11 @@ __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             acc[i][j] = mfma32x32x16(av[q][i], bv[q][j], acc[i][j]);
-            const int u = (h2 * 2 + q) * 8 + i * 2 + j;
+            const int u = (h2 * 2 + q) * (2 * MI) + i * 2 + j;
             if (u < LS && refill) dma(s + NS - 1, na, nb, u);
           }
     }
@@ -239,14 +251,14 @@ __device__ __forceinline__ void g256_tile(const G256Args& p, const int tm, const
   // epilogue: lane holds rows 8 (r / 4) + 4 hf + r % 4 of each 32-row block
   // and column l32 of each 32-column block
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn * 64 + j * 32 + l32;
       if (n >= p.n) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t mb = m0 + wm * 128 + i * 32 + 8 * g + 4 * hf;
+        const int64_t mb = m0 + wm * (BM / 2) + i * 32 + 8 * g + 4 * hf;
         if constexpr (OUT == kOutBf16) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
@@ -306,11 +318,11 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, in
   *tn = (t % per_group) / gm;
 }
 
-template <int OUT, int KB>
+template <int OUT, int KB, int BM>
 __global__ __launch_bounds__(kThreads, 1) void g256_kernel(const G256Args p, int64_t a_bs,
                                                            int64_t a2_bs, int64_t b_bs,
                                                            int64_t y_bs) {
-  const int tiles_m = static_cast<int>((p.m + kBM - 1) / kBM);
+  const int tiles_m = static_cast<int>((p.m + BM - 1) / BM);
   const int tiles_n = (p.n + kBN - 1) / kBN;
   int tm, tn;
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, &tm, &tn);
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void g256_kernel(const G256Args p, int
   q.a2 = p.a2 ? p.a2 + b * a2_bs : nullptr;
   q.b = p.b + b * b_bs;
   q.y = static_cast<char*>(p.y) + b * y_bs * (OUT == kOutBf16 ? 2 : 4);
-  g256_tile<OUT, KB>(q, tm, tn);
+  g256_tile<OUT, KB, BM>(q, tm, tn);
 }
 
 // The warmup statistics of one batch entry (layer) per blockIdx.y from
@@ -376,16 +388,16 @@ __global__ __launch_bounds__(kThreads, 1) void gram_t_kernel(const GramTArgs p, 
   q.ldy = p.h;
   q.sym = job != 1;
   q.zero_first = p.zero_first;
-  g256_tile<kAccF32, KB>(q, tm, tn);
+  g256_tile<kAccF32, KB, kBM>(q, tm, tn);
 }
 
 // Buffer-load offsets are 32 bit: rows of A run in blocks whose bytes stay
 // below 2^31 (a launch each); B must fit below 2^31 bytes as a whole.
-template <int OUT>
+template <int OUT, int BM = kBM>
 hipError_t launch_g256(G256Args a, int batch, int64_t a_bs, int64_t b_bs, int64_t y_bs,
                        hipStream_t stream) {
   const int64_t row_bytes = a.lda * 2;
-  const int64_t max_rows = (static_cast<int64_t>(INT32_MAX) / row_bytes) / kBM * kBM;
+  const int64_t max_rows = (static_cast<int64_t>(INT32_MAX) / row_bytes) / BM * BM;
   if (max_rows == 0 || static_cast<int64_t>(a.n) * a.ldb * 2 > INT32_MAX)
     return hipErrorInvalidValue;
   if (batch == 0 || a.m == 0 || a.n == 0) return hipSuccess;
@@ -396,8 +408,8 @@ hipError_t launch_g256(G256Args a, int batch, int64_t a_bs, int64_t b_bs, int64_
     blk.a = a.a + r0 * a.lda;
     if (a.a2) blk.a2 = a.a2 + r0 * a.lda;
     blk.y = static_cast<char*>(a.y) + r0 * a.ldy * ys;
-    const int64_t tiles = ((blk.m + kBM - 1) / kBM) * ((a.n + kBN - 1) / kBN);
-    hipLaunchKernelGGL((g256_kernel<OUT, kStageK>), dim3(static_cast<unsigned>(tiles), batch),
+    const int64_t tiles = ((blk.m + BM - 1) / BM) * ((a.n + kBN - 1) / kBN);
+    hipLaunchKernelGGL((g256_kernel<OUT, kStageK, BM>), dim3(static_cast<unsigned>(tiles), batch),
                        dim3(kThreads), 0, stream, blk, a_bs, a_bs, b_bs, y_bs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -408,7 +420,7 @@ hipError_t launch_g256(G256Args a, int batch, int64_t a_bs, int64_t b_bs, int64_
 }  // namespace
 
 hipError_t launch_g256_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
-                            int h_in, int h_out, hipStream_t stream) {
+                            int h_in, int h_out, hipStream_t stream, int row_tile) {
   G256Args a{};
   a.a = x;
   a.b = w;
@@ -418,6 +430,7 @@ hipError_t launch_g256_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, i
   a.k = h_in;
   a.y = y;
   a.ldy = h_out;
+  if (row_tile == 192) return launch_g256<kOutBf16, 192>(a, 1, 0, 0, 0, stream);
   return launch_g256<kOutBf16>(a, 1, 0, 0, 0, stream);
 }
 

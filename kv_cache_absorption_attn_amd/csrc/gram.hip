@@ -432,17 +432,23 @@ static double round_fill(int64_t tiles, int cus) {
 hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, int h_in,
                           int h_out, hipStream_t stream) {
   if (nt_gemm256_supported(h_in)) {
-    // 256 x 256 tiles run each FLOP ~1.4x faster than 256 x 128 ones (fewer
-    // operand bytes and barriers per MFMA) but come in half the number:
-    // take them when that still wins after the partial last round
+    // Three tilings: 256 x 128, 192 x 256 and 256 x 256 run a FLOP 1, 1.28
+    // and 1.41 times as fast (fewer operand bytes and barriers per MFMA;
+    // measured at a contraction of 5120) but come in fewer, larger tiles.
+    // Take the one whose rate times its fill of the rounds of one tile per CU
+    // is highest: e.g. 4680 x 5120 outputs are 760, 500 and 380 tiles on
+    // 256 CUs, 99 %, 98 % and 74 % of whole rounds, and 192 x 256 wins.
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidDevice;
-    const int64_t rows = (n + 255) / 256;
-    const double big = 1.4 * round_fill(rows * ((h_out + 255) / 256), cus);
-    const double small = round_fill(rows * ((h_out + 127) / 128), cus);
-    if (big > small) return launch_g256_bf16(x, w, y, n, h_in, h_out, stream);
+    const int64_t rows256 = (n + 255) / 256, rows192 = (n + 191) / 192;
+    const int64_t cols256 = (h_out + 255) / 256, cols128 = (h_out + 127) / 128;
+    const double r128 = round_fill(rows256 * cols128, cus);
+    const double r192 = 1.28 * round_fill(rows192 * cols256, cus);
+    const double r256 = 1.41 * round_fill(rows256 * cols256, cus);
+    if (r256 >= r192 && r256 > r128) return launch_g256_bf16(x, w, y, n, h_in, h_out, stream, 256);
+    if (r192 > r128) return launch_g256_bf16(x, w, y, n, h_in, h_out, stream, 192);
     return launch_nt_gemm256_bf16(x, w, y, n, h_in, h_out, stream);
   }
   const int64_t tiles = ((n + kT - 1) / kT) * ((h_out + kT - 1) / kT);

@@ -241,9 +241,11 @@ hipError_t launch_project(const uint16_t* x, const uint16_t* w, uint16_t* y, int
 
 // The 256 x 256-tile NT GEMM (gemm256.hip).
 // Y = X W^T, bf16 out; contraction length a multiple of 8 (any length works;
-// the last stage is masked).
+// the last stage is masked). row_tile 256 or 192: the tile height (the rows
+// of X a workgroup covers; 192-row tiles fit more row counts into whole
+// rounds of the chip).
 hipError_t launch_g256_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n,
-                            int h_in, int h_out, hipStream_t stream);
+                            int h_in, int h_out, hipStream_t stream, int row_tile = 256);
 // Y[b] = (hi[b] + lo[b]) W[b]^T in fp32 for h x h operands (an fp32 matrix
 // held as two bf16 planes times a bf16 matrix).
 hipError_t launch_g256_split_f32(const uint16_t* hi, const uint16_t* lo, const uint16_t* w,

@@ -418,7 +418,8 @@ def test_apply_bit_exact():
 
 
 @pytest.mark.parametrize("n,h_in,h_out", [(200, 128, 192), (4680, 1536, 1536), (7, 64, 64),
-                                         (4680, 5120, 5120), (1000, 200, 72)])
+                                         (4680, 5120, 5120), (1000, 200, 72), (4700, 5120, 4096),
+                                         (4680, 5088, 5120)])
 def test_project(n, h_in, h_out):
     log(f"project {n}x{h_in}->{h_out}")
     x = wl.random_bf16((n, h_in), 0.5, 51)
