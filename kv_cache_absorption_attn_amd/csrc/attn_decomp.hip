@@ -2,7 +2,9 @@
 //
 // One pass over a chunk's queries produces the local-only result (sink frame
 // plus current frames), the history-only result and, by merging their
-// log-sum-exp states, the full-history result and D = O_full - O_local.
+// log-sum-exp states, the full-history result and D = O_full - O_local. The
+// history may come in two pieces (the two ranges of a ring buffer that has
+// wrapped); attention does not depend on the order of its keys.
 // ISPA paper ("Towards Memory-Efficient Autoregressive Video Generation via
 // Instance-Specific Parametric Absorption"): §3.1 item 1 (A_loc over current
 // and sink tokens, A_full over the whole history, collected during warmup),

@@ -5,9 +5,10 @@
 // lowest take W_new = W + dW in place).
 //
 // The blocked Cholesky factors G + lambda I one 128-column block at a time:
-// this file holds the diagonal-block factorisation (in LDS, with the inverse
-// of the factor for the GEMM-based panel and triangular solves); the panel
-// and trailing updates are fp32 MFMA GEMMs.
+// this file holds the diagonal-block factorisation (register-blocked, with
+// the inverse of the factor for the GEMM-based panel and triangular solves),
+// the probes that decide which layers' solves are refined, and the small
+// elementwise pieces; the panel and trailing updates are fp32 MFMA GEMMs.
 
 #include <float.h>
 
