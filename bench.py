@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import csv
 import hashlib
+import re
 import json
 import math
 import os
@@ -524,11 +525,21 @@ def gram_deferred_measure(ispa, w: wl.Workload, reps: int = 5, seed: int = 5):
             "resident_activation_gb_per_layer": round(2 * T * n * h * 2 / 1e9, 3)}
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed, so that
+    a change to comments or layout alone keeps the hash of the code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernel: str) -> str:
+    """sha256 (first 16 hex digits) of the code of the sources a kernel is
+    built from, comments and whitespace aside."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -599,7 +610,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, w: wl.Workload):
         f"Calibration: the plain 1 GiB copy (the last large copy of the run) reads FETCH_SIZE = {fc:.0f} KiB "
         f"and WRITE_SIZE = {wc:.0f} KiB, so fetch counts are scaled by {f_fac:.4f} and write counts "
         f"by {w_fac:.4f}.", "",
-        "| kernel | source sha256[:16] | launches | fetch GB/launch | write GB/launch | "
+        "| kernel | code sha256[:16] (comments aside) | launches | fetch GB/launch | write GB/launch | "
         "bytes/launch (fetch+write) |",
         "|---|---|---:|---:|---:|---:|",
     ]
