@@ -335,9 +335,38 @@ __global__ __launch_bounds__(kThreads, 1) void g256_kernel(const G256Args p, int
   g256_tile<OUT, KB, BM>(q, tm, tn);
 }
 
+// Tile u of a lower triangle of nt x nt tiles in grouped order: groups of
+// kGroupM tile rows, each swept column by column over the tiles on or below
+// the diagonal, so that consecutive tiles share row panels as in
+// grouped_tile (row-major order would give a window of consecutive tiles in
+// the last rows one column panel per tile).
+__device__ __forceinline__ void tri_grouped_tile(int u, int nt, int* tm, int* tn) {
+  int r0 = 0, gm = 0;
+  for (;; r0 += kGroupM) {
+    gm = nt - r0 < kGroupM ? nt - r0 : kGroupM;
+    const int cnt = gm * r0 + gm * (gm + 1) / 2;
+    if (u < cnt) break;
+    u -= cnt;
+  }
+  if (u < gm * r0) {   // columns left of the group's diagonal block: gm tiles each
+    *tn = u / gm;
+    *tm = r0 + u % gm;
+    return;
+  }
+  u -= gm * r0;        // the diagonal block: column r0 + j holds gm - j tiles
+  int j = 0;
+  while (u >= gm - j) {
+    u -= gm - j;
+    ++j;
+  }
+  *tn = r0 + j;
+  *tm = r0 + j + u;
+}
+
 // The warmup statistics of one batch entry (layer) per blockIdx.y from
 // feature-major X^T, D^T [h][ld]: the G tiles (lower triangle of 256-tiles,
-// mirrored), the C tiles (all) and the E tiles (lower triangle, mirrored).
+// mirrored), the C tiles (all) and the E tiles (lower triangle, mirrored),
+// each in an order whose consecutive tiles share operand panels.
 struct GramTArgs {
   const uint16_t* xt;
   const uint16_t* dt;
@@ -358,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void gram_t_kernel(const GramTArgs p, 
   const int64_t b = blockIdx.y;
   const int n_sym = nt * (nt + 1) / 2;
   const int64_t hh = static_cast<int64_t>(p.h) * p.h;
-  // order: C tiles (grouped), then G, then E (lower triangles, row-major)
+  // order: C tiles (grouped), then G, then E (lower triangles, grouped)
   int job, tm, tn;
   if (t < nt * nt) {
     job = 1;
@@ -367,12 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void gram_t_kernel(const GramTArgs p, 
     int u = t - nt * nt;
     job = u < n_sym ? 0 : 2;
     if (u >= n_sym) u -= n_sym;
-    tm = 0;
-    while (u > tm) {
-      u -= tm + 1;
-      ++tm;
-    }
-    tn = u;
+    tri_grouped_tile(u, nt, &tm, &tn);
   }
   G256Args q{};
   const uint16_t* xb = p.xt + b * p.in_bs;
