@@ -6,10 +6,17 @@
 //
 // Tile 128 x 128 per workgroup, k-stage 16, 4 waves of 64 x 64 (2 x 2 MFMA
 // blocks of 32 x 32). Operands are staged k-major in LDS (As[k][m], Bs[k][n])
-// from either storage order, converting bf16 operands to fp32 on the way.
+// from either storage order, converting bf16 operands to fp32 on the way,
+// through two register sets, so that a stage's loads are issued two stages
+// before its MFMAs. At most 128 VGPRs and 34 KB of LDS per workgroup keep
+// four workgroups (four waves a SIMD) on a CU: the kernel lives on that
+// occupancy (k-stages of 32, two workgroups a CU, ran 0.75x; three a CU
+// 0.9x).
 // The whole k range of an output tile is consumed before its epilogue writes,
 // so a GEMM whose single tile row (M <= 128) or tile column (N <= 128) covers
 // the operand region it overwrites may run in place.
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "ispa_internal.h"
@@ -102,7 +109,7 @@ struct TileLoader {
 };
 
 template <bool AKC, bool ABF, bool BKC, bool BBF>
-__global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(const GemmF32Params p) {
+__global__ __launch_bounds__(kThreads, 4) void gemm_f32_kernel(const GemmF32Params p) {
   __shared__ __attribute__((aligned(16))) float As[2][kTK * kLd];
   __shared__ __attribute__((aligned(16))) float Bs[2][kTK * kLd];
 
@@ -122,8 +129,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(const GemmF32Para
   const int64_t a_srow = p.a_s0, a_sk = p.a_s1;
   const int64_t b_srow = p.b_s1, b_sk = p.b_s0;
 
-  TileLoader<AKC, ABF> la;
-  TileLoader<BKC, BBF> lb;
+  // two register sets of operand tiles: stage ks + 2 is loaded while stage
+  // ks is multiplied and stage ks + 1 waits in the other set for its store,
+  // so a load has two stages of MFMA work to arrive
+  TileLoader<AKC, ABF> la[2];
+  TileLoader<BKC, BBF> lb[2];
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -131,21 +141,27 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(const GemmF32Para
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int nk = (p.K + kTK - 1) / kTK;
-  la.load(Abase, a_srow, a_sk, tm * kTM, p.M, 0, p.K, tid);
-  lb.load(Bbase, b_srow, b_sk, tn * kTN, p.N, 0, p.K, tid);
-  la.store(As[0], tid);
-  lb.store(Bs[0], tid);
+  la[0].load(Abase, a_srow, a_sk, tm * kTM, p.M, 0, p.K, tid);
+  lb[0].load(Bbase, b_srow, b_sk, tn * kTN, p.N, 0, p.K, tid);
+  if (nk > 1) {
+    la[1].load(Abase, a_srow, a_sk, tm * kTM, p.M, kTK, p.K, tid);
+    lb[1].load(Bbase, b_srow, b_sk, tn * kTN, p.N, kTK, p.K, tid);
+  }
+  la[0].store(As[0], tid);
+  lb[0].store(Bs[0], tid);
   __syncthreads();
 
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    const bool has_next = ks + 1 < nk;
-    if (has_next) {
-      la.load(Abase, a_srow, a_sk, tm * kTM, p.M, (ks + 1) * kTK, p.K, tid);
-      lb.load(Bbase, b_srow, b_sk, tn * kTN, p.N, (ks + 1) * kTK, p.K, tid);
+  // stage ks from LDS slot S = ks % 2; register set S held it and takes stage
+  // ks + 2, set S ^ 1 holds stage ks + 1 and goes to the other slot, which
+  // every wave finished reading before the previous barrier
+  auto step = [&](int ks, auto s_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;
+    if (ks + 2 < nk) {
+      la[S].load(Abase, a_srow, a_sk, tm * kTM, p.M, (ks + 2) * kTK, p.K, tid);
+      lb[S].load(Bbase, b_srow, b_sk, tn * kTN, p.N, (ks + 2) * kTK, p.K, tid);
     }
-    const float* as = As[buf];
-    const float* bs = Bs[buf];
+    const float* as = As[S];
+    const float* bs = Bs[S];
 #pragma unroll
     for (int kk = 0; kk < kTK / 2; ++kk) {
       const int k = 2 * kk + hf;
@@ -159,11 +175,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(const GemmF32Para
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x2f32(a[i], bv[j], acc[i][j]);
     }
-    if (has_next) {
-      la.store(As[buf ^ 1], tid);
-      lb.store(Bs[buf ^ 1], tid);
+    if (ks + 1 < nk) {
+      la[S ^ 1].store(As[S ^ 1], tid);
+      lb[S ^ 1].store(Bs[S ^ 1], tid);
     }
     __syncthreads();
+  };
+  for (int ks = 0; ks < nk; ks += 2) {
+    step(ks, std::integral_constant<int, 0>{});
+    if (ks + 1 < nk) step(ks + 1, std::integral_constant<int, 1>{});
   }
 
 #pragma unroll
