@@ -290,7 +290,7 @@ def _synthetic_stats(L, h, n, seed):
 
 
 @pytest.mark.parametrize("L,h,n", [(1, 128, 300), (3, 320, 500), (2, 64, 50), (2, 256, 400),
-                                   (2, 200, 300)])
+                                   (2, 200, 300), (2, 136, 300), (1, 160, 250)])
 def test_ridge_and_score(L, h, n):
     log(f"ridge L={L} h={h} n={n}")
     lam = 1e-2
