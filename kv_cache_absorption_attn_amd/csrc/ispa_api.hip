@@ -90,12 +90,16 @@ inline int blk_row(int b, int h) { return b * kCholBlock < h ? b * kCholBlock : 
 
 // Right-hand sides of the triangular solves: per layer an h x nc fp32 matrix
 // (row stride nc) at R + layer * stride; layers whose mask entry is 0 are
-// left untouched (no mask: all layers).
+// left untouched (no mask: all layers). lower: the right-hand side is lower
+// triangular (the identity, for L^-1), so a forward solve keeps row block
+// [r0, r2) zero from column r2 on and the products skip those columns (the
+// columns they would touch are exact zeros either way: same results).
 struct Rhs {
   float* R;
   int nc;
   int64_t stride;
   const int* mask;
+  bool lower = false;
 };
 
 // Rows of blocks [ba, bb) of the right-hand sides <- L^-1 R for the
@@ -109,15 +113,15 @@ hipError_t solve_lower(int ba, int bb, const RidgeWs& w, const Rhs& r, int h, in
     float* rk = r.R + static_cast<int64_t>(r0) * r.nc;
     const float* linv = w.Linv + static_cast<int64_t>(r0) * kCholBlock;
     const int nbk = r2 - r0;
-    return gemm(nbk, r.nc, nbk, linv, kCholBlock, 1, lb, false, rk, r.nc, 1, r.stride, false, rk,
-                r.nc, r.stride, 1.f, 0.f, L, false, s, r.mask);
+    return gemm(nbk, r.lower ? r2 : r.nc, nbk, linv, kCholBlock, 1, lb, false, rk, r.nc, 1,
+                r.stride, false, rk, r.nc, r.stride, 1.f, 0.f, L, false, s, r.mask);
   }
   const int bm = (ba + bb) / 2, r1 = blk_row(bm, h);
   hipError_t e = solve_lower(ba, bm, w, r, h, L, s);
   if (e != hipSuccess) return e;
   // R[r1:r2] -= L[r1:r2, r0:r1] R[r0:r1]
-  e = gemm(r2 - r1, r.nc, r1 - r0, w.L + static_cast<int64_t>(r1) * h + r0, h, 1, hh, false,
-           r.R + static_cast<int64_t>(r0) * r.nc, r.nc, 1, r.stride, false,
+  e = gemm(r2 - r1, r.lower ? r1 : r.nc, r1 - r0, w.L + static_cast<int64_t>(r1) * h + r0, h, 1,
+           hh, false, r.R + static_cast<int64_t>(r0) * r.nc, r.nc, 1, r.stride, false,
            r.R + static_cast<int64_t>(r1) * r.nc, r.nc, r.stride, -1.f, 1.f, L, false, s, r.mask);
   if (e != hipSuccess) return e;
   return solve_lower(bm, bb, w, r, h, L, s);
@@ -731,7 +735,7 @@ int ispa_drift_prepare(int n_layers, int h, const float* G, float lambda, int64_
   ISPA_TRY(ispa::launch_copy_add_diag(G, w.L, h, n_layers, lambda, s));
   ISPA_TRY(cholesky(0, nblk, w, h, n_layers, info, s));
   ISPA_TRY(ispa::launch_identity(linv, h, n_layers, s));
-  ISPA_TRY(solve_lower(0, nblk, w, Rhs{linv, h, hh, nullptr}, h, n_layers, s));
+  ISPA_TRY(solve_lower(0, nblk, w, Rhs{linv, h, hh, nullptr, true}, h, n_layers, s));
   // ||L^{-1}||_F^2 = tr((G + lambda I)^{-1}) -> (h - lambda tr) / n_warm
   ISPA_TRY(ispa::launch_drift_sum(linv, h, h, h, hh, n_layers, w.part, h, lambda,
                                   static_cast<double>(n_warm), nullptr, ref, s));
@@ -753,7 +757,7 @@ int ispa_drift_prepare_factored(int n_layers, int h, float lambda, int64_t n_war
   const int nblk = (h + kCholBlock - 1) / kCholBlock;
   const int64_t hh = static_cast<int64_t>(h) * h;
   ISPA_TRY(ispa::launch_identity(linv, h, n_layers, s));
-  ISPA_TRY(solve_lower(0, nblk, w, Rhs{linv, h, hh, nullptr}, h, n_layers, s));
+  ISPA_TRY(solve_lower(0, nblk, w, Rhs{linv, h, hh, nullptr, true}, h, n_layers, s));
   ISPA_TRY(ispa::launch_drift_sum(linv, h, h, h, hh, n_layers, w.part, h, lambda,
                                   static_cast<double>(n_warm), nullptr, ref, s));
   return ISPA_OK;
